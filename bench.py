@@ -1,0 +1,275 @@
+#!/usr/bin/env python3
+"""Benchmark: attention forward + backward TFLOPS on one MI355X.
+
+Workload (one "step"): fa_fwd then the three launches of the backward
+(fa_bwd_stage 1, 2, 3 = fa_bwd) on B=8, H=16, N=4096, d=128, bf16, causal,
+with inputs already resident in HBM. Counted FLOPs: 4*B*H*N^2*d for the
+forward, halved for causal, and 2.5x that for the backward.
+
+Prints ONE JSON line on stdout. Besides the contract fields it carries
+  roofline     -- for the kernel with the largest average duration, its
+                  counted FLOPs / its HIP-event-timed duration against the
+                  bf16 dense MFMA peak; traffic from the committed rocprofv3
+                  PMC summary if it was taken on the current kernel source;
+  cpu_baseline -- the float64 CPU oracle timed on a bounded sample of heads
+                  of the same workload (reported, never a target);
+  breakdown    -- per-launch times and TFLOPS.
+`--suite PATH` additionally times every workload of the parity suite and
+writes one JSON line per workload to PATH.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16/fp16 MFMA
+PEAK_FP8_TFLOPS = 5033.2    # MI355X dense fp8 MFMA
+KERNEL_SOURCES = {
+    "fwd_mfma_kernel": "exact_io_aware_54_amd/csrc/fa_fwd.hip",
+    "bwd_main_kernel": "exact_io_aware_54_amd/csrc/fa_bwd.hip",
+    "fwd_fp8_kernel": "exact_io_aware_54_amd/csrc/fa_fwd_fp8.hip",
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def counted_flops(B, H, N, d, causal, backward=False):
+    f = 4.0 * B * H * N * N * d * (0.5 if causal else 1.0)
+    return 2.5 * f if backward else f
+
+
+def source_sha(kernel):
+    path = os.path.join(ROOT, KERNEL_SOURCES[kernel])
+    h = hashlib.sha256()
+    for p in (path, os.path.join(ROOT, "exact_io_aware_54_amd/csrc/fa_device.h")):
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel):
+    """HBM bytes per launch from the committed PMC summary, or None if stale/absent."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))[kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha") != source_sha(kernel):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(q, k, v, do, scale, causal, budget_s, max_heads=16):
+    """Time the float64 oracle on whole heads of the workload until budget_s is spent."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()
+                     if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        cores = 1
+    B, H, N, d = q.shape
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    rng = np.random.default_rng(0)
+    order = rng.permutation(len(heads))
+    done, t0 = 0, time.perf_counter()
+    for idx in order[:max_heads]:
+        b, h = heads[idx]
+        f64 = [t[b, h].float().numpy().astype(np.float64) for t in (q, k, v, do)]
+        oracle.attention_forward(f64[0], f64[1], f64[2], scale, causal)
+        oracle.attention_backward(f64[0], f64[1], f64[2], f64[3], scale, causal)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    secs = time.perf_counter() - t0
+    flops = done * 3.5 * counted_flops(1, 1, N, d, causal)
+    return {"value": flops / secs / 1e12, "unit": "TFLOPS", "cores": cores, "kind": "oracle",
+            "sample": f"fwd+bwd of {done} whole heads (N={N}, d={d}, causal) of the same "
+                      f"workload in float64 numpy, {secs:.1f} s"}
+
+
+def time_launches(fns, steps, warmup, torch):
+    """Run `fns` in order per step; event-time each; return (wall_ms_per_step, [avg ms per fn])."""
+    for _ in range(warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s in range(steps):
+        evs[s][0].record(stream)
+        for i, f in enumerate(fns):
+            f()
+            evs[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    per = [sum(evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(steps)) / steps
+           for i in range(len(fns))]
+    return wall, per
+
+
+def run_main(args):
+    import torch
+    import exact_io_aware_54_amd as fa
+    from exact_io_aware_54_amd import inputs
+
+    fa.load_library()
+    B, H, N, d, causal = 8, 16, 4096, 128, True
+    scale = 1.0 / math.sqrt(d)
+    print(f"[bench] drawing inputs B{B} H{H} N{N} d{d}", file=sys.stderr, flush=True)
+    q, k, v, do = inputs.draw_qkv(B, H, N, d, inputs.SEEDS["train_4k"], torch.bfloat16, with_do=True)
+    qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
+    o = torch.empty_like(qd)
+    lse = torch.empty((B, H, N), device="cuda", dtype=torch.float32)
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    ws = fa.workspace_for(qd)
+
+    fns = [lambda: fa.fa_fwd(qd, kd, vd, o, lse, scale, causal)]
+    for stage in (1, 2, 3):
+        fns.append(lambda s=stage: fa.fa_bwd_stage(s, qd, kd, vd, o, lse, dod, dq, dk, dv, ws,
+                                                   scale, causal))
+    print(f"[bench] warmup {args.warmup}, timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    wall_ms, per = time_launches(fns, args.steps, args.warmup, torch)
+    fwd_ms, pre_ms, main_ms, conv_ms = per
+    f_fwd = counted_flops(B, H, N, d, causal)
+    f_bwd = counted_flops(B, H, N, d, causal, backward=True)
+    value = (f_fwd + f_bwd) / (wall_ms * 1e-3) / 1e12
+    bwd_ms = pre_ms + main_ms + conv_ms
+
+    if main_ms >= fwd_ms:
+        kname, kflops, kms = "bwd_main_kernel", f_bwd, main_ms
+    else:
+        kname, kflops, kms = "fwd_mfma_kernel", f_fwd, fwd_ms
+    achieved = kflops / (kms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": kname, "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic_for(kname), "avg_launch_ms": round(kms, 4),
+                "counted_flops_per_launch": kflops}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print(f"[bench] cpu baseline (~{args.cpu_seconds:.0f} s of oracle work)", file=sys.stderr,
+              flush=True)
+        cpu = cpu_baseline(q, k, v, do, scale, causal, args.cpu_seconds)
+
+    line = {
+        "metric": "attention fwd+bwd TFLOPS (bf16, d=128, N=4K-16K) and % of MFMA peak, 1 GPU",
+        "value": round(value, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall_ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "fwd+bwd causal attention, B=8 H=16 N=4096 d=128 bf16",
+                   "B": B, "H": H, "N": N, "d": d, "causal": causal, "global_batch": B,
+                   "seq_len": N, "parallelism": "none (1 GPU)"},
+        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "breakdown": {
+            "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+            "bwd_stage_ms": {"pre": round(pre_ms, 4), "main": round(main_ms, 4),
+                             "dq_convert": round(conv_ms, 4)},
+            "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2),
+            "bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2),
+            "fwd_frac_peak": round(f_fwd / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "bwd_frac_peak": round(f_bwd / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        },
+    }
+    print(json.dumps(line), flush=True)
+    if args.suite:
+        run_suite(args.suite, torch, fa, inputs)
+
+
+def run_suite(path, torch, fa, inputs):
+    """Median and minimum of 20 timed launches (after 5 warm-ups) for every workload."""
+    import statistics
+    cases = [
+        ("fwd bf16 B4 H16 N2048 d64", "fwd", torch.bfloat16, 4, 16, 2048, 64, False, "fwd_bf16"),
+        ("fwd bf16 B4 H16 N2000 d64 (ragged)", "fwd", torch.bfloat16, 4, 16, 2000, 64, False,
+         "fwd_bf16_ragged"),
+        ("fwd bf16 causal B1 H32 N8192 d128", "fwd", torch.bfloat16, 1, 32, 8192, 128, True,
+         "causal_8k"),
+        ("fwd bf16 causal B1 H32 N16384 d128", "fwd", torch.bfloat16, 1, 32, 16384, 128, True,
+         "causal_16k"),
+        ("fwd bf16 causal B8 H16 N4096 d128", "fwd", torch.bfloat16, 8, 16, 4096, 128, True,
+         "train_4k"),
+        ("bwd bf16 causal B8 H16 N4096 d128", "bwd", torch.bfloat16, 8, 16, 4096, 128, True,
+         "train_4k"),
+        ("fwd fp8 B2 H32 N8192 d128", "fp8", None, 2, 32, 8192, 128, False, "fp8_8k"),
+        ("fwd f32 B1 H2 N128 d64", "fwd", torch.float32, 1, 2, 128, 64, False, "tiny_f32"),
+    ]
+    out = open(path, "w")
+    for name, kind, dt, B, H, N, d, causal, seedkey in cases:
+        print(f"[suite] {name}", file=sys.stderr, flush=True)
+        scale = d ** -0.5
+        seed = inputs.SEEDS[seedkey]
+        if kind == "fp8":
+            (q8, k8, v8), sc = inputs.draw_fp8(B, H, N, d, seed)
+            q8, k8, v8 = q8.cuda(), k8.cuda(), v8.cuda()
+            o = torch.empty((B, H, N, d), device="cuda", dtype=torch.bfloat16)
+            lse = torch.empty((B, H, N), device="cuda", dtype=torch.float32)
+            fn = lambda: fa.fa_fwd_fp8(q8, k8, v8, sc[0], sc[1], sc[2], o, lse, scale, causal)  # noqa
+            flops, peak = counted_flops(B, H, N, d, causal), PEAK_FP8_TFLOPS
+        else:
+            q, k, v, do = (t.cuda() for t in inputs.draw_qkv(B, H, N, d, seed, dt, with_do=True))
+            o = torch.empty_like(q)
+            lse = torch.empty((B, H, N), device="cuda", dtype=torch.float32)
+            fa.fa_fwd(q, k, v, o, lse, scale, causal)
+            if kind == "fwd":
+                fn = lambda: fa.fa_fwd(q, k, v, o, lse, scale, causal)  # noqa
+                flops = counted_flops(B, H, N, d, causal)
+            else:
+                dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+                ws = fa.workspace_for(q)
+                fn = lambda: fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, scale, causal)  # noqa
+                flops = counted_flops(B, H, N, d, causal, backward=True)
+            peak = PEAK_BF16_TFLOPS
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(20):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        med, mn = statistics.median(times), min(times)
+        rec = {"workload": name, "median_ms": round(med, 4), "min_ms": round(mn, 4),
+               "tflops_median": round(flops / (med * 1e-3) / 1e12, 2),
+               "frac_peak_median": round(flops / (med * 1e-3) / 1e12 / peak, 4), "seed": seed}
+        print(json.dumps(rec), file=out, flush=True)
+        print(f"[suite] {json.dumps(rec)}", file=sys.stderr, flush=True)
+        del fn
+        torch.cuda.empty_cache()
+    out.close()
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="budget for the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--suite", metavar="PATH", help="also time every workload, JSON lines to PATH")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: attention shards by (batch, head) with no "
+              "communication, so the whole-job rate at N GPUs is N times the 1-GPU figure at "
+              "the per-GPU head count; run with --gpus 1.", file=sys.stderr, flush=True)
+        sys.exit(2)
+    run_main(args)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,216 @@
+"""Exact scaled-dot-product attention on AMD MI355X (gfx950), FlashAttention-style.
+
+The computation lives in ``libfa.so`` (hand-written HIP kernels behind the C
+ABI declared in ``include/fa.h``). This module is a thin ctypes binding with
+the same entry-point names: it checks that torch tensors match the shapes the
+C ABI will assume, passes their device pointers and the current HIP stream,
+and raises ``FAError`` on a non-zero status. Every step of the attention runs
+in the library's kernels; there is no fallback path. If the library has not
+been built, calls raise ``RuntimeError``.
+
+Entry points: ``fa_fwd``, ``fa_fwd_fp8``, ``fa_bwd``, ``fa_bwd_stage``,
+``fa_bwd_workspace_bytes``,
+``fa_status_string``, ``fa_version``; ``forward`` / ``backward`` /
+``forward_fp8`` allocate outputs with torch and call them.
+"""
+
+import ctypes
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
+
+FA_F32, FA_F16, FA_BF16 = 0, 1, 2
+FA_OK = 0
+STATUS = {
+    0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_DTYPE",
+    -4: "FA_ERR_HEADDIM", -5: "FA_ERR_WORKSPACE", -6: "FA_ERR_HIP", -7: "FA_ERR_ARG",
+}
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({fa_status_string(status)})")
+
+
+def load_library(path=None):
+    """Load libfa.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(f"libfa.so not found at {path}; build it with "
+                           "`python -m exact_io_aware_54_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_fwd.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+    lib.fa_fwd.restype = i
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, f, f, f, vp, vp, i, i, i, i, f, i, vp]
+    lib.fa_fwd_fp8.restype = i
+    lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
+    lib.fa_bwd_workspace_bytes.restype = sz
+    lib.fa_bwd.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, vp]
+    lib.fa_bwd.restype = i
+    lib.fa_bwd_stage.argtypes = [i] + lib.fa_bwd.argtypes
+    lib.fa_bwd_stage.restype = i
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_version.argtypes = []
+    lib.fa_version.restype = i
+    _lib = lib
+    return lib
+
+
+def fa_status_string(status):
+    return load_library().fa_status_string(int(status)).decode()
+
+
+def fa_version():
+    return load_library().fa_version()
+
+
+# ------------------------------------------------------------------ marshalling
+
+def _dtype_code(t):
+    import torch
+    codes = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check_bhnd(name, t, shape, dtype=None):
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype} != {dtype}")
+
+
+def _raise(fn, st):
+    if st != FA_OK:
+        raise FAError(fn, st)
+
+
+def fa_fwd(q, k, v, o, lse, scale, causal, stream=None):
+    """Enqueue O = softmax(scale q k^T [causal]) v and LSE into ``o`` / ``lse``."""
+    import torch
+    lib = load_library()
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _check_bhnd(name, t, (B, H, N, d), q.dtype)
+    _check_bhnd("lse", lse, (B, H, N), torch.float32)
+    st = lib.fa_fwd(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                    B, H, N, d, float(scale), int(bool(causal)), _stream(stream))
+    _raise("fa_fwd", st)
+
+
+def fa_fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, o, lse, scale, causal, stream=None):
+    """FP8 forward: q8/k8/v8 are uint8 E4M3 codes; o is bfloat16."""
+    import torch
+    lib = load_library()
+    B, H, N, d = q8.shape
+    for name, t in (("q8", q8), ("k8", k8), ("v8", v8)):
+        _check_bhnd(name, t, (B, H, N, d), torch.uint8)
+    _check_bhnd("o", o, (B, H, N, d), torch.bfloat16)
+    _check_bhnd("lse", lse, (B, H, N), torch.float32)
+    st = lib.fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), float(q_descale), float(k_descale),
+                        float(v_descale), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
+                        int(bool(causal)), _stream(stream))
+    _raise("fa_fwd_fp8", st)
+
+
+def fa_bwd_workspace_bytes(B, H, N, d):
+    return int(load_library().fa_bwd_workspace_bytes(B, H, N, d))
+
+
+def fa_bwd(q, k, v, o, lse, do, dq, dk, dv, workspace, scale, causal, stream=None):
+    """Enqueue dQ, dK, dV of <O, dO>; ``workspace`` is a uint8 device tensor."""
+    import torch
+    lib = load_library()
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do), ("dq", dq),
+                    ("dk", dk), ("dv", dv)):
+        _check_bhnd(name, t, (B, H, N, d), q.dtype)
+    _check_bhnd("lse", lse, (B, H, N), torch.float32)
+    if workspace.dtype != torch.uint8 or not workspace.is_cuda:
+        raise TypeError("workspace must be a uint8 device tensor")
+    st = lib.fa_bwd(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                    _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
+                    B, H, N, d, float(scale), int(bool(causal)), _stream(stream))
+    _raise("fa_bwd", st)
+
+
+def fa_bwd_stage(stage, q, k, v, o, lse, do, dq, dk, dv, workspace, scale, causal, stream=None):
+    """Enqueue one of fa_bwd's three launches (1 preprocess, 2 main, 3 dQ convert)."""
+    import torch
+    lib = load_library()
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do), ("dq", dq),
+                    ("dk", dk), ("dv", dv)):
+        _check_bhnd(name, t, (B, H, N, d), q.dtype)
+    _check_bhnd("lse", lse, (B, H, N), torch.float32)
+    if workspace.dtype != torch.uint8 or not workspace.is_cuda:
+        raise TypeError("workspace must be a uint8 device tensor")
+    st = lib.fa_bwd_stage(int(stage), _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                          _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                          workspace.numel(), B, H, N, d, float(scale), int(bool(causal)),
+                          _stream(stream))
+    _raise("fa_bwd_stage", st)
+
+
+# ------------------------------------------------- allocate-and-call conveniences
+
+def forward(q, k, v, scale=None, causal=False):
+    """Allocate O and LSE with torch and run fa_fwd. Returns (o, lse)."""
+    import torch
+    scale = q.shape[-1] ** -0.5 if scale is None else scale
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:-1], device=q.device, dtype=torch.float32)
+    fa_fwd(q, k, v, o, lse, scale, causal)
+    return o, lse
+
+
+def forward_fp8(q8, k8, v8, descales, scale=None, causal=False):
+    import torch
+    scale = q8.shape[-1] ** -0.5 if scale is None else scale
+    o = torch.empty(q8.shape, device=q8.device, dtype=torch.bfloat16)
+    lse = torch.empty(q8.shape[:-1], device=q8.device, dtype=torch.float32)
+    fa_fwd_fp8(q8, k8, v8, descales[0], descales[1], descales[2], o, lse, scale, causal)
+    return o, lse
+
+
+def workspace_for(q):
+    import torch
+    B, H, N, d = q.shape
+    return torch.empty(fa_bwd_workspace_bytes(B, H, N, d), device=q.device, dtype=torch.uint8)
+
+
+def backward(q, k, v, o, lse, do, scale=None, causal=False, workspace=None):
+    """Allocate dQ, dK, dV (and a workspace if none is given) and run fa_bwd."""
+    import torch
+    scale = q.shape[-1] ** -0.5 if scale is None else scale
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = workspace_for(q) if workspace is None else workspace
+    fa_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, scale, causal)
+    return dq, dk, dv

@@ -1,0 +1,127 @@
+// C ABI of libfa (declared in include/fa.h): argument validation, dispatch on
+// (dtype, head dim, causal) and launch on the caller's stream. Nothing is
+// launched when an argument is invalid.
+
+#include "../../include/fa.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "fa_launch.h"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+int check_shape(int B, int H, int N, int d) {
+    if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+    const int64_t total = (int64_t)B * H * N * d;
+    if (total >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
+    return FA_OK;
+}
+
+bool good_scale(float s) { return isfinite(s) && s > 0.f; }
+
+int status_of(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+int fa_version(void) { return kVersion; }
+
+const char* fa_status_string(int status) {
+    switch (status) {
+        case FA_OK: return "ok";
+        case FA_ERR_NULL: return "a required pointer is NULL";
+        case FA_ERR_SHAPE: return "invalid shape (B, H, N must be >= 1 and B*H*N*d < 2^31)";
+        case FA_ERR_DTYPE: return "dtype not supported by this entry point";
+        case FA_ERR_HEADDIM: return "head dim not supported";
+        case FA_ERR_WORKSPACE: return "workspace too small";
+        case FA_ERR_HIP: return "HIP runtime error at launch";
+        case FA_ERR_ARG: return "invalid scalar argument (scale or descale)";
+        default: return "unknown status";
+    }
+}
+
+int fa_fwd(int dtype, const void* q, const void* k, const void* v, void* o, float* lse, int B,
+           int H, int N, int d, float scale, int causal, hipStream_t stream) {
+    if (!q || !k || !v || !o) return FA_ERR_NULL;
+    if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+    const int st = check_shape(B, H, N, d);
+    if (st != FA_OK) return st;
+    if (!good_scale(scale)) return FA_ERR_ARG;
+    const int BH = B * H;
+    if (dtype == FA_F32)
+        return status_of(fa::launch_fwd_f32(d, causal != 0, static_cast<const float*>(q),
+                                            static_cast<const float*>(k),
+                                            static_cast<const float*>(v), static_cast<float*>(o),
+                                            lse, BH, N, scale, stream));
+    return status_of(
+        fa::launch_fwd_mfma(dtype, d, causal != 0, q, k, v, o, lse, BH, N, scale, stream));
+}
+
+int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, float q_descale, float k_descale,
+               float v_descale, void* o_bf16, float* lse, int B, int H, int N, int d,
+               float scale, int causal, hipStream_t stream) {
+    if (!q8 || !k8 || !v8 || !o_bf16) return FA_ERR_NULL;
+    const int st = check_shape(B, H, N, d);
+    if (st != FA_OK) return st;
+    if (d != 128) return FA_ERR_HEADDIM;
+    if (!good_scale(scale) || !good_scale(q_descale) || !good_scale(k_descale) ||
+        !good_scale(v_descale))
+        return FA_ERR_ARG;
+    const float qk = scale * q_descale * k_descale;
+    if (!good_scale(qk)) return FA_ERR_ARG;
+    return status_of(fa::launch_fwd_fp8(d, causal != 0, q8, k8, v8, qk, v_descale, o_bf16, lse,
+                                        B * H, N, stream));
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
+    if (check_shape(B, H, N, d) != FA_OK) return 0;
+    const size_t rows = (size_t)B * H * N;
+    return align256(rows * d * sizeof(float)) + align256(rows * sizeof(float));
+}
+
+namespace {
+int bwd_common(int dtype, const void* q, const void* k, const void* v, const void* o,
+               const float* lse, const void* dO, void* dq, void* dk, void* dv, void* workspace,
+               size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
+               int stages, hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
+    if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+    const int st = check_shape(B, H, N, d);
+    if (st != FA_OK) return st;
+    if (!good_scale(scale)) return FA_ERR_ARG;
+    if (workspace_bytes < fa_bwd_workspace_bytes(B, H, N, d)) return FA_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255) != 0) return FA_ERR_WORKSPACE;
+    const size_t rows = (size_t)B * H * N;
+    float* dq_acc = static_cast<float*>(workspace);
+    float* delta = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                            align256(rows * d * sizeof(float)));
+    return status_of(fa::launch_bwd(dtype, d, causal != 0, q, k, v, o, lse, dO, dq, dk, dv,
+                                    dq_acc, delta, B * H, N, scale, stages, stream));
+}
+}  // namespace
+
+int fa_bwd(int dtype, const void* q, const void* k, const void* v, const void* o,
+           const float* lse, const void* dO, void* dq, void* dk, void* dv, void* workspace,
+           size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
+           hipStream_t stream) {
+    return bwd_common(dtype, q, k, v, o, lse, dO, dq, dk, dv, workspace, workspace_bytes, B, H, N,
+                      d, scale, causal, 7, stream);
+}
+
+int fa_bwd_stage(int stage, int dtype, const void* q, const void* k, const void* v,
+                 const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                 void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                 float scale, int causal, hipStream_t stream) {
+    if (stage < 1 || stage > 3) return FA_ERR_ARG;
+    return bwd_common(dtype, q, k, v, o, lse, dO, dq, dk, dv, workspace, workspace_bytes, B, H, N,
+                      d, scale, causal, 1 << (stage - 1), stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,93 @@
+// Device-side building blocks for the gfx950 attention kernels: vector types,
+// MFMA wrappers, wavefront reductions, conversions and the workgroup->tile map.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Element type traits: the 8-wide operand vector of one 32x32x16 MFMA.
+template <typename T> struct Vec;
+template <> struct Vec<__bf16> { typedef bf16x8 x8; typedef bf16x4 x4; };
+template <> struct Vec<_Float16> { typedef f16x8 x8; typedef f16x4 x4; };
+
+// D = A * B + C on a 32x32 tile with K = 16 (bf16 / fp16 inputs, fp32 acc).
+// Operand lane layout: lane l supplies row (A) or column (B) l % 32 and eight
+// K values from half l / 32; the same (half, slot) pairs are contracted, so
+// any K order is valid as long as A and B use the same one.
+// Accumulator layout: lane l holds column l % 32, register r holds row
+// 8 * (r / 4) + 4 * (l / 32) + r % 4.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+// fp8 (OCP E4M3) x fp8 -> fp32, 32x32 tile, K = 64; 32 bytes per lane per
+// operand. Format code 0 selects E4M3 for both operands; the E8M0 block
+// scales are fixed at 127 (= 2^0).
+__device__ __forceinline__ f32x16 mfma32_fp8(i32x8 a, i32x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// Row of the 32x32 accumulator held in register r by a lane of half `h`.
+__device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+// Value of lane l ^ 32 (the other half of the wavefront) combined with max/+.
+__device__ __forceinline__ float wave_half_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float wave_half_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Pack 8 floats from accumulator registers [base, base + 8) into one operand.
+template <typename T>
+__device__ __forceinline__ typename Vec<T>::x8 pack8(const f32x16& a, int base) {
+    typename Vec<T>::x8 r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = (T)a[base + j];
+    return r;
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+// L2). Remap the hardware id so that every XCD receives a contiguous range of
+// logical ids; tiles that share K/V (same head) then share an L2.
+__device__ __forceinline__ int xcd_remap(int id, int G) {
+    const int per = (G + 7) >> 3;          // ids per XCD, rounded up
+    const int tall = G - (per - 1) * 8;    // XCDs that receive `per` ids
+    const int x = id & 7, loc = id >> 3;
+    return x < tall ? x * per + loc : tall * per + (x - tall) * (per - 1) + loc;
+}
+
+// When a 32x32 accumulator is reused as an MFMA operand, registers r..r+7 of
+// a lane in half h hold rows {4h..4h+3} and {8+4h..8+4h+3} of a 16-row group
+// (see acc_row). The other operand, read from LDS as 8 contiguous elements at
+// slot 8h, must present the same rows in the same order, so row w (0..15) of
+// the group is stored at position acc_kperm16(w): groups of four rows go to
+// positions 0, 8, 4, 12.
+__device__ __forceinline__ int acc_kperm16(int kk) {
+    const int g4 = kk >> 2, i = kk & 3;
+    const int pos4 = (g4 == 1) ? 2 : (g4 == 2) ? 1 : g4;   // 0,2,1,3
+    return pos4 * 4 + i;
+}
+
+}  // namespace fa

@@ -1,0 +1,23 @@
+// Host-side launchers of the attention kernels (internal to libfa).
+// Arguments are validated by the C ABI layer before these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+hipError_t launch_fwd_mfma(int dtype, int d, bool causal, const void* q, const void* k,
+                           const void* v, void* o, float* lse, int BH, int N, float scale,
+                           hipStream_t stream);
+hipError_t launch_fwd_f32(int d, bool causal, const float* q, const float* k, const float* v,
+                          float* o, float* lse, int BH, int N, float scale, hipStream_t stream);
+hipError_t launch_fwd_fp8(int d, bool causal, const void* q8, const void* k8, const void* v8,
+                          float qk_scale, float v_descale, void* o, float* lse, int BH, int N,
+                          hipStream_t stream);
+hipError_t launch_bwd(int dtype, int d, bool causal, const void* q, const void* k, const void* v,
+                      const void* o, const float* lse, const void* dO, void* dq, void* dk,
+                      void* dv, float* dq_acc, float* delta, int BH, int N, float scale,
+                      int stages, hipStream_t stream);  // stages: bit 0 pre, 1 main, 2 dQ convert
+
+}  // namespace fa

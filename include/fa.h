@@ -1,0 +1,149 @@
+/*
+ * fa.h -- C ABI of libfa: exact scaled-dot-product attention on AMD MI355X
+ * (gfx950), computed the IO-aware FlashAttention way.
+ *
+ * What is computed. For every (batch b, head h), with S = scale * Q K^T:
+ *   O   = softmax(S) V                       ("11.11 Flash Attention",
+ *                                            section "Standard Attention: Step
+ *                                            by Step": the attention formula)
+ *   LSE_i = ln sum_j exp(S_ij)               (the per-row statistics m and l of
+ *                                            the online softmax, folded into
+ *                                            one number, LSE = m + ln l; the
+ *                                            zenaique.com page's follow-up on
+ *                                            how the backward avoids storing P)
+ * The N x N matrices S and P are never written to memory: Q, K and V are
+ * tiled on chip and an online softmax keeps a running row max and row sum
+ * (same page, sections "Flash Attention: The Key Insight" and "The Tiling
+ * Algorithm"); the loop order is Q blocks outer, K/V blocks inner, with the
+ * grid parallel over batch x heads x query blocks (section "Flash Attention
+ * 2"). The backward recomputes the score tiles from Q, K, V and LSE (section
+ * "The Recomputation Trade-off").
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor arguments are DEVICE pointers, allocated and owned by the
+ *    caller. The library allocates no memory and keeps no per-call state.
+ *  - Layout: contiguous row-major [B, H, N, d] for Q, K, V, O, dO, dQ, dK, dV;
+ *    LSE is [B, H, N] float32 (natural log, of the scaled scores).
+ *  - d must be 64 or 128. B, H, N >= 1 and B*H*N*d < 2^31.
+ *  - causal != 0: query i attends to keys 0..i (the mask is not on the pages;
+ *    it is the usual lower-triangular mask with N_q = N_k).
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *    and returns without waiting. FA_OK means "launched", not "finished".
+ *  - Every argument is validated before anything is launched; on an error
+ *    nothing is enqueued and a negative fa_status is returned.
+ *  - Calls are thread-safe; calls that share output buffers on one stream are
+ *    ordered by the stream.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA_F32 = 0,  /* float32 */
+    FA_F16 = 1,  /* IEEE half */
+    FA_BF16 = 2  /* bfloat16 */
+} fa_dtype;
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_NULL = -1,       /* a required pointer is NULL                      */
+    FA_ERR_SHAPE = -2,      /* B, H or N < 1, or the tensor is too large         */
+    FA_ERR_DTYPE = -3,      /* dtype not supported by this entry point           */
+    FA_ERR_HEADDIM = -4,    /* d not in {64, 128}                                */
+    FA_ERR_WORKSPACE = -5,  /* workspace smaller than fa_bwd_workspace_bytes()   */
+    FA_ERR_HIP = -6,        /* the HIP runtime reported an error at launch       */
+    FA_ERR_ARG = -7         /* a scalar argument is invalid (scale not finite or
+                               not positive, descale not finite or <= 0)         */
+} fa_status;
+
+/*
+ * Forward pass: O = softmax(scale * Q K^T [causal mask]) V and LSE.
+ *   dtype  FA_BF16 / FA_F16: MFMA matrix cores with float32 accumulation, P
+ *          rounded to the input type before the P V product, O rounded to
+ *          nearest even on store.
+ *          FA_F32: float32 arithmetic throughout (no reduced-precision step).
+ *   q, k, v  [B,H,N,d] of `dtype`, read only.
+ *   o        [B,H,N,d] of `dtype`, written.
+ *   lse      [B,H,N] float32, written; may be NULL if not wanted.
+ *   scale    > 0 and finite; the usual value is 1/sqrt(d).
+ */
+int fa_fwd(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/*
+ * FP8 forward ("11.11 Flash Attention", section "Flash Attention 3": FP8
+ * attention). Inputs are OCP FP8 E4M3 codes (1 byte each) with one float32
+ * descale per tensor: the real value of Q is q8 * q_descale, and likewise for
+ * K and V. S = scale * q_descale * k_descale * (Q8 K8^T) is formed by the fp8
+ * MFMA with float32 accumulation; P is scaled by 2^8 and rounded to E4M3 for
+ * the P V product; O is written as bfloat16.
+ *   q8, k8, v8  [B,H,N,d] uint8 E4M3 codes, read only.
+ *   o_bf16      [B,H,N,d] bfloat16, written.  lse [B,H,N] float32 or NULL.
+ *   d must be 128 for this entry point (FA_ERR_HEADDIM otherwise).
+ */
+int fa_fwd_fp8(const void* q8, const void* k8, const void* v8,
+               float q_descale, float k_descale, float v_descale,
+               void* o_bf16, float* lse,
+               int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/*
+ * Size in bytes of the scratch buffer fa_bwd needs: a float32 dQ accumulator
+ * [B,H,N,d] plus the float32 row terms D_i = sum_k dO_ik O_ik [B,H,N]. Returns
+ * 0 for invalid shapes.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * Backward pass: given dO, returns dQ, dK, dV of L = <O, dO>.
+ * The score tiles are recomputed from Q, K and LSE (P_ij = exp(S_ij - LSE_i)),
+ * so no N x N matrix is stored ("11.11 Flash Attention", section "The
+ * Recomputation Trade-off"). With D_i = sum_k dO_ik O_ik:
+ *   dV = P^T dO,  dS = P * (dO V^T - D),  dQ = scale dS K,  dK = scale dS^T Q.
+ *   dtype      FA_BF16 or FA_F16 (FA_ERR_DTYPE for FA_F32).
+ *   q, k, v, o, dO  [B,H,N,d] of `dtype`; o is the forward output.
+ *   lse        [B,H,N] float32 from fa_fwd with the same scale and causal flag.
+ *   dq, dk, dv [B,H,N,d] of `dtype`, written.
+ *   workspace  device scratch of at least fa_bwd_workspace_bytes(B,H,N,d)
+ *              bytes, 256-byte aligned; overwritten (no initial value needed).
+ * The dQ accumulation uses float32 atomics, so dQ may differ in the last bits
+ * from run to run; dK and dV are deterministic.
+ */
+int fa_bwd(int dtype, const void* q, const void* k, const void* v, const void* o,
+           const float* lse, const void* dO, void* dq, void* dk, void* dv,
+           void* workspace, size_t workspace_bytes,
+           int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/*
+ * One of the three launches that make up fa_bwd, for callers that time or
+ * schedule them separately. Same arguments and validation as fa_bwd, plus
+ *   stage 1: D_i = sum_k dO_ik O_ik into the workspace, and the workspace's
+ *            float32 dQ accumulator set to zero;
+ *   stage 2: the main kernel -- recompute P and dS tile by tile, write dK and
+ *            dV, add scale * dS K into the dQ accumulator (float32 atomics);
+ *   stage 3: convert the dQ accumulator to `dtype` into dq.
+ * Calling stages 1, 2, 3 in order on one stream is exactly fa_bwd. Stage 2
+ * needs stage 1's workspace contents; stage 3 needs stage 2's. Any other
+ * stage value returns FA_ERR_ARG.
+ */
+int fa_bwd_stage(int stage, int dtype, const void* q, const void* k, const void* v,
+                 const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                 void* workspace, size_t workspace_bytes,
+                 int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/* Human-readable text for a fa_status value (static storage, never NULL). */
+const char* fa_status_string(int status);
+
+/* Library ABI version: major * 10000 + minor * 100 + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */
