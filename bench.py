@@ -120,6 +120,14 @@ def run_main(args):
     from exact_io_aware_54_amd import inputs
 
     fa.load_library()
+    if args.calibrate_copy:
+        # a plain copy of known size: reads and writes exactly 1 GiB each
+        src = torch.ones(1 << 28, device="cuda", dtype=torch.float32)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     B, H, N, d, causal = 8, 16, 4096, 128, True
     scale = 1.0 / math.sqrt(d)
     print(f"[bench] drawing inputs B{B} H{H} N{N} d{d}", file=sys.stderr, flush=True)
@@ -261,6 +269,9 @@ def main():
                     help="budget for the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--suite", metavar="PATH", help="also time every workload, JSON lines to PATH")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain 1 GiB device copy, the reference kernel for scaling "
+                         "PMC byte counters")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

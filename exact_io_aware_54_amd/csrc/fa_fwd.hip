@@ -5,7 +5,7 @@
 // block of one (batch, head) and walks the K/V blocks in order (section
 // "Flash Attention 2": Q-block outer loop, parallel over batch x heads x query
 // blocks). Each K/V tile is staged once in LDS and shared by the four
-// wavefronts. Per tile: scores, running row max, exponentials against the new
+// wavefronts. Per tile: scores, running row max, exponentials against the
 // max, rescaled running sum and rescaled output (sections "Flash Attention:
 // The Key Insight" and "The Tiling Algorithm"). The output stays unnormalised
 // and is divided by the row sum once at the end (the reduced non-matmul work
@@ -18,12 +18,18 @@
 //    reduction plus one exchange with the other half of the wave
 //    (v_permlane32_swap). m and l are one register each.
 //  * The probabilities P^T, converted to 16-bit, are fed straight back as the
-//    B operand of O^T = V^T P^T; V is transposed into LDS (with the row order
-//    of the accumulator layout) when it is staged, so every MFMA operand read
-//    is one 16-byte LDS load.
+//    B operand of O^T = V^T P^T.
+//  * K and V tiles go HBM -> LDS with global_load_lds_dwordx4 (no VGPR
+//    staging, no VALU), double-buffered: the next tile's loads are issued
+//    before the current tile is computed. Both are stored row-major with an
+//    XOR swizzle of the 16-byte chunks so that the MFMA operand reads are
+//    free of bank conflicts. K is read as 16-byte rows; V^T is read with
+//    ds_read_b64_tr_b16, which transposes 4x4 blocks of 16-bit elements
+//    across lanes on the way out of LDS.
 //  * Softmax works in base 2: p = 2^(s * scale * log2 e - m) via v_exp_f32.
-//  * K/V tiles are double-buffered: the next tile's global loads are in flight
-//    while the current tile is computed, then written to the other buffer.
+//    The running max is refreshed only when a row's max grows by more than
+//    2^8 (then O and l are rescaled); otherwise p stays <= 2^8 against the
+//    stale max. This is exact: m, l and O always use the same reference.
 //  * Causal: tiles past the block's last query are never visited, a wave
 //    skips tiles wholly above its own rows, and only tiles that straddle the
 //    diagonal (or the ragged end of N) pay for the mask.
@@ -36,72 +42,225 @@
 namespace fa {
 namespace {
 
-template <typename T, int D>
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+template <int D>
 struct FwdTile {
-    static constexpr int BM = 128;          // queries per workgroup (4 waves x 32)
-    static constexpr int BN = 64;           // keys per K/V tile
-    static constexpr int NT = 256;          // threads per workgroup
-    static constexpr int KSTR = D + 8;      // LDS row stride of K (elements, +16 B pad)
-    static constexpr int VSTR = BN + 8;     // LDS row stride of V^T (elements, +16 B pad)
-    static constexpr int KS = D / 16;       // MFMA k-steps over the head dim
-    static constexpr int DB = D / 32;       // 32-row blocks of O^T
-    static constexpr int KCH = BN * D / 8 / NT;   // 16-byte K chunks per thread
-    static constexpr int VKG = BN * D / 8 / NT;   // keys per thread in the V transpose
-    static constexpr int DCH = D / 8;             // 16-byte chunks per row
+    static constexpr int BM = 128;                 // queries per workgroup (4 waves x 32)
+    static constexpr int BN = 64;                  // keys per K/V tile
+    static constexpr int NT = 256;                 // threads per workgroup
+    static constexpr int ROWB = D * 2;             // bytes per K/V row
+    static constexpr int CH = D / 8;               // 16-byte chunks per row
+    static constexpr int RPB = 256 / ROWB;         // rows per 256 bytes (one pass of banks)
+    static constexpr int TILEB = BN * ROWB;        // bytes per K (or V) tile
+    static constexpr int NLOAD = TILEB / (NT * 16);  // direct loads per thread per tile
+    static constexpr int KS = D / 16;              // MFMA k-steps over the head dim
+    static constexpr int DB = D / 32;              // 32-row blocks of O^T
 };
 
-template <typename T, int D>
-struct KVStage {
-    using C = FwdTile<T, D>;
-    using V8 = typename Vec<T>::x8;
-    V8 k[C::KCH];
-    V8 v[C::VKG];
+// Chunk swizzles (chunk index within a row -> stored position).
+// K rows are read 16 consecutive rows x one chunk at a time: XOR with the row.
+template <int D>
+__device__ __forceinline__ int kswz(int r) {
+    using C = FwdTile<D>;
+    return (r / C::RPB) % C::CH;
+}
+// V rows are read 4 rows x 4 chunks at a time (transposing reads): spread
+// the four rows over the four 64-byte quarters of the banks.
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+    using C = FwdTile<D>;
+    return 4 * ((r / C::RPB) % (C::CH / 4));
+}
 
-    __device__ __forceinline__ void load(const T* Kh, const T* Vh, int kbase, int N, int tid) {
+constexpr float kRescaleThreshold = 8.f;  // log2 units: refresh m when it grows by > 2^8
+constexpr int kVmcntZero = 0x0F70;        // s_waitcnt vmcnt(0), expcnt/lgkmcnt untouched
+
+// Per-wavefront state of the forward kernel and its steps.
+template <typename T, int D, bool CAUSAL>
+struct FwdWave {
+    using C = FwdTile<D>;
+    using V8 = typename Vec<T>::x8;
+    using V4 = typename Vec<T>::x4;
+
+    const T* Kh;
+    const T* Vh;
+    int N, nkt, tid, wave, lane, h, l32, q0, qrow;
+    float c;
+    V8 qf[C::KS];               // B operand of S^T = K Q^T (d = 16 s + 8 h + j)
+    int ld_row[C::NLOAD], ld_kcol[C::NLOAD], ld_vcol[C::NLOAD];
+    int koff[2][C::KS];         // LDS byte offsets of the K operand reads
+    int voff[4][2][C::DB];      // LDS byte offsets of the V^T transposing reads
+    float m_run, l_run;         // running (reference) max of s * c and this lane's sum
+    f32x16 oacc[C::DB];         // O^T accumulators (head dim 32 b + row, query = lane)
+
+    __device__ __forceinline__ void init(const T* Qh, const T* Kh_, const T* Vh_, int N_,
+                                         int qb, float c_) {
+        Kh = Kh_;
+        Vh = Vh_;
+        N = N_;
+        c = c_;
+        tid = threadIdx.x;
+        lane = tid & 63;
+        wave = tid >> 6;
+        l32 = lane & 31;
+        h = lane >> 5;
+        q0 = qb * C::BM + wave * 32;
+        qrow = q0 + l32;
+        const V8* src = reinterpret_cast<const V8*>(Qh + (size_t)min(qrow, N - 1) * D + 8 * h);
 #pragma unroll
-        for (int i = 0; i < C::KCH; ++i) {
-            const int id = tid + C::NT * i;
-            const int row = id / C::DCH, col = (id % C::DCH) * 8;
-            const int key = kbase + row;
-            if (key < N) k[i] = *reinterpret_cast<const V8*>(Kh + (size_t)key * D + col);
-            else k[i] = V8{};
+        for (int s = 0; s < C::KS; ++s) qf[s] = src[2 * s];
+        const int q_last = min(N, (qb + 1) * C::BM) - 1;
+        nkt = CAUSAL ? (q_last / C::BN + 1) : (N + C::BN - 1) / C::BN;
+
+        // Direct-load map: load i of this thread fills LDS bytes [i*4096 +
+        // tid*16, +16) of a tile, i.e. row r, stored chunk position p; it
+        // fetches global chunk p ^ swz(r) of that row (rows past N re-read row
+        // N-1; their scores are masked).
+#pragma unroll
+        for (int i = 0; i < C::NLOAD; ++i) {
+            const int byte = i * (C::NT * 16) + tid * 16;
+            const int r = byte / C::ROWB, p = (byte % C::ROWB) / 16;
+            ld_row[i] = r;
+            ld_kcol[i] = (p ^ kswz<D>(r)) * 8;
+            ld_vcol[i] = (p ^ vswz<D>(r)) * 8;
         }
-        const int c = tid % C::DCH, g = tid / C::DCH;
+        // K (A side of S^T): key 32 c2 + l32, chunk 2 s + h.
 #pragma unroll
-        for (int i = 0; i < C::VKG; ++i) {
-            const int key = kbase + g * C::VKG + i;
-            if (key < N) v[i] = *reinterpret_cast<const V8*>(Vh + (size_t)key * D + c * 8);
-            else v[i] = V8{};
+        for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+            for (int s = 0; s < C::KS; ++s) {
+                const int r = 32 * c2 + l32;
+                koff[c2][s] = r * C::ROWB + 16 * ((2 * s + h) ^ kswz<D>(r));
+            }
+        // V^T (A side of O^T = V^T P^T) via transposing reads. Read `half` of
+        // key group g, head-dim block b: this lane supplies row 16 g + 8 half +
+        // 4 h + (lane % 16) / 4, columns 32 b + 16 ((lane / 16) % 2) + 4 (lane %
+        // 4) .. +3; it receives head dim 32 b + lane % 32 at keys 16 g + 8 half
+        // + 4 h + 0..3 -- the key order of its probabilities in P^T.
+        const int src_r = 4 * h + (lane & 15) / 4;
+        const int src_d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int b = 0; b < C::DB; ++b) {
+                    const int r = 16 * g + 8 * hf + src_r;
+                    const int d = 32 * b + src_d;
+                    voff[g][hf][b] = r * C::ROWB + 16 * ((d / 8) ^ vswz<D>(r)) + 2 * (d % 8);
+                }
+        m_run = -INFINITY;
+        l_run = 0.f;
+#pragma unroll
+        for (int b = 0; b < C::DB; ++b) oacc[b] = f32x16{};
+    }
+
+    __device__ __forceinline__ void issue_tile(int kbase, char* sKd, char* sVd) const {
+#pragma unroll
+        for (int i = 0; i < C::NLOAD; ++i) {
+            const size_t row = (size_t)min(kbase + ld_row[i], N - 1) * D;
+            char* kdst = sKd + i * (C::NT * 16) + wave * 1024;
+            char* vdst = sVd + i * (C::NT * 16) + wave * 1024;
+            __builtin_amdgcn_global_load_lds(Kh + row + ld_kcol[i], kdst, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(Vh + row + ld_vcol[i], vdst, 16, 0, 0);
         }
     }
 
-    __device__ __forceinline__ void store(T* sK, T* sV, int tid) const {
+    // One K/V tile: wait for it, start the next one into the other buffers,
+    // then scores, online softmax and P V on this one.
+    __device__ __forceinline__ void step(int kt, const char* kb, const char* vb, char* kn,
+                                         char* vn) {
+        const int kbase = kt * C::BN;
+        // tile kt has landed in LDS (this thread's direct loads done, then the
+        // barrier for everyone's), and the other buffers are no longer read
+        __builtin_amdgcn_s_waitcnt(kVmcntZero);
+        __syncthreads();
+        if (kt + 1 < nkt) issue_tile(kbase + C::BN, kn, vn);
+
+        const bool active = !CAUSAL || kbase <= q0 + 31;
+        if (!active) return;
+        f32x16 s[2];
+        s[0] = f32x16{};
+        s[1] = f32x16{};
 #pragma unroll
-        for (int i = 0; i < C::KCH; ++i) {
-            const int id = tid + C::NT * i;
-            const int row = id / C::DCH, col = (id % C::DCH) * 8;
-            *reinterpret_cast<V8*>(sK + row * C::KSTR + col) = k[i];
-        }
-        // V^T[d][key]: this thread holds VKG consecutive keys x 8 consecutive d.
-        const int c = tid % C::DCH, g = tid / C::DCH;
-        const int key0 = g * C::VKG;
-        const int pos = (key0 & ~15) + acc_kperm16(key0 & 15);
+        for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
-        for (int dd = 0; dd < 8; ++dd) {
-            T* dst = sV + (c * 8 + dd) * C::VSTR + pos;
-            if constexpr (C::VKG == 4) {
-                typename Vec<T>::x4 w;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) w[i] = v[i][dd];
-                *reinterpret_cast<typename Vec<T>::x4*>(dst) = w;
-            } else {
-                static_assert(C::VKG == 2, "V transpose handles 2 or 4 keys per thread");
-                typedef __attribute__((__vector_size__(2 * sizeof(T)))) T x2;
-                x2 w;
-                w[0] = v[0][dd];
-                w[1] = v[1][dd];
-                *reinterpret_cast<x2*>(dst) = w;
+            for (int c2 = 0; c2 < 2; ++c2) {
+                const V8 a = *reinterpret_cast<const V8*>(kb + koff[c2][ks]);
+                s[c2] = mfma32(a, qf[ks], s[c2]);
             }
+        // mask: key kbase + 32 c2 + acc_row(r, h) is visible iff it is <= lim + 4 h + kbase
+        const bool need_mask = (kbase + C::BN > N) || (CAUSAL && kbase + C::BN - 1 > q0);
+        if (need_mask) {
+            const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - kbase - 4 * h;
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (32 * c2 + 8 * (r >> 2) + (r & 3) > lim) s[c2][r] = -INFINITY;
+        }
+        float mx = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+        for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+        mx = wave_half_max(mx) * c;
+        if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleThreshold) != 0) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = fast_exp2(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int b = 0; b < C::DB; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
+        }
+        float rs = 0.f;
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = fast_exp2(fmaf(s[c2][r], c, -m_run));
+                s[c2][r] = p;
+                rs += p;
+            }
+        l_run += rs;
+
+        V8 pf[4];
+        pf[0] = pack8<T>(s[0], 0);
+        pf[1] = pack8<T>(s[0], 8);
+        pf[2] = pack8<T>(s[1], 0);
+        pf[3] = pack8<T>(s[1], 8);
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int b = 0; b < C::DB; ++b) {
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + voff[g][0][b]));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + voff[g][1][b]));
+                const s16x4 w[2] = {lo, hi};
+                V8 a;
+                __builtin_memcpy(&a, w, sizeof(a));
+                oacc[b] = mfma32(a, pf[g], oacc[b]);
+            }
+    }
+
+    __device__ __forceinline__ void finish(T* Oh, float* lse_h) {
+        const float lt = wave_half_sum(l_run);
+        if (qrow < N) {
+            const float inv = 1.f / lt;
+            T* orow = Oh + (size_t)qrow * D;
+#pragma unroll
+            for (int b = 0; b < C::DB; ++b)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    V4 w;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) w[i] = (T)(oacc[b][4 * r4 + i] * inv);
+                    *reinterpret_cast<V4*>(orow + 32 * b + 8 * r4 + 4 * h) = w;
+                }
+            if (lse_h != nullptr && h == 0) lse_h[qrow] = (m_run + log2f(lt)) * kLn2;
         }
     }
 };
@@ -110,144 +269,34 @@ template <typename T, int D, bool CAUSAL>
 __global__ void __launch_bounds__(256, 2)
 fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                 T* __restrict__ O, float* __restrict__ LSE, int BH, int N, int nqb, float c) {
-    using C = FwdTile<T, D>;
-    using V8 = typename Vec<T>::x8;
-    using V4 = typename Vec<T>::x4;
-    __shared__ __attribute__((aligned(16))) T sK[2][C::BN * C::KSTR];
-    __shared__ __attribute__((aligned(16))) T sV[2][D * C::VSTR];
+    using C = FwdTile<D>;
+    // Two buffers per tensor as four separate LDS objects: the compiler can
+    // then tell that the loads in flight into one buffer never alias the
+    // reads of the other, and does not wait for them before every read.
+    __shared__ __attribute__((aligned(1024))) char sK0[C::TILEB];
+    __shared__ __attribute__((aligned(1024))) char sK1[C::TILEB];
+    __shared__ __attribute__((aligned(1024))) char sV0[C::TILEB];
+    __shared__ __attribute__((aligned(1024))) char sV1[C::TILEB];
 
     const int L = xcd_remap(blockIdx.x, BH * nqb);
     const int bh = L / nqb;
     const int qb = CAUSAL ? (nqb - 1 - L % nqb) : (L % nqb);
     const size_t head = (size_t)bh * N * D;
-    const T* Qh = Q + head;
-    const T* Kh = K + head;
-    const T* Vh = V + head;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l32 = lane & 31, h = lane >> 5;
-    const int q0 = qb * C::BM + wave * 32;  // first query row of this wave
-    const int qrow = q0 + l32;              // query held by this lane
-
-    // B operand of S^T = K Q^T: slot (h, j) of k-step s is d = 16 s + 8 h + j.
-    V8 qf[C::KS];
-    if (qrow < N) {
-        const V8* src = reinterpret_cast<const V8*>(Qh + (size_t)qrow * D + 8 * h);
-#pragma unroll
-        for (int s = 0; s < C::KS; ++s) qf[s] = src[2 * s];
-    } else {
-#pragma unroll
-        for (int s = 0; s < C::KS; ++s) qf[s] = V8{};
+    FwdWave<T, D, CAUSAL> w;
+    w.init(Q + head, K + head, V + head, N, qb, c);
+    w.issue_tile(0, sK0, sV0);
+    for (int kt = 0; kt < w.nkt; kt += 2) {
+        w.step(kt, sK0, sV0, sK1, sV1);
+        if (kt + 1 < w.nkt) w.step(kt + 1, sK1, sV1, sK0, sV0);
     }
-
-    const int q_last = min(N, (qb + 1) * C::BM) - 1;
-    const int nkt = CAUSAL ? (q_last / C::BN + 1) : (N + C::BN - 1) / C::BN;
-
-    KVStage<T, D> st;
-    st.load(Kh, Vh, 0, N, tid);
-    st.store(sK[0], sV[0], tid);
-    __syncthreads();
-
-    float m_run = -INFINITY;  // running max of s * c (base-2 units)
-    float l_run = 0.f;        // this lane's share of the running sum
-    f32x16 oacc[C::DB];
-#pragma unroll
-    for (int b = 0; b < C::DB; ++b) oacc[b] = f32x16{};
-
-    for (int kt = 0; kt < nkt; ++kt) {
-        const int buf = kt & 1;
-        const bool more = kt + 1 < nkt;
-        const int kbase = kt * C::BN;
-        if (more) st.load(Kh, Vh, kbase + C::BN, N, tid);
-
-        const bool active = !CAUSAL || kbase <= q0 + 31;
-        if (active) {
-            const T* kb = sK[buf];
-            f32x16 s[2];
-            s[0] = f32x16{};
-            s[1] = f32x16{};
-#pragma unroll
-            for (int ks = 0; ks < C::KS; ++ks) {
-#pragma unroll
-                for (int c2 = 0; c2 < 2; ++c2) {
-                    const V8 a = *reinterpret_cast<const V8*>(kb + (32 * c2 + l32) * C::KSTR + 16 * ks + 8 * h);
-                    s[c2] = mfma32(a, qf[ks], s[c2]);
-                }
-            }
-            const bool need_mask = (kbase + C::BN > N) || (CAUSAL && kbase + C::BN - 1 > q0);
-            if (need_mask) {
-#pragma unroll
-                for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = kbase + 32 * c2 + acc_row(r, h);
-                        if (key >= N || (CAUSAL && key > qrow)) s[c2][r] = -INFINITY;
-                    }
-            }
-            float mx = s[0][0];
-#pragma unroll
-            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-            mx = wave_half_max(mx);
-            const float m_new = fmaxf(m_run, mx * c);
-            const float alpha = fast_exp2(m_run - m_new);
-            float rs = 0.f;
-#pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float p = fast_exp2(fmaf(s[c2][r], c, -m_new));
-                    s[c2][r] = p;
-                    rs += p;
-                }
-            l_run = l_run * alpha + rs;
-            m_run = m_new;
-#pragma unroll
-            for (int b = 0; b < C::DB; ++b)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
-
-            V8 pf[4];
-            pf[0] = pack8<T>(s[0], 0);
-            pf[1] = pack8<T>(s[0], 8);
-            pf[2] = pack8<T>(s[1], 0);
-            pf[3] = pack8<T>(s[1], 8);
-            const T* vb = sV[buf];
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-#pragma unroll
-                for (int b = 0; b < C::DB; ++b) {
-                    const V8 a = *reinterpret_cast<const V8*>(vb + (32 * b + l32) * C::VSTR + 16 * g + 8 * h);
-                    oacc[b] = mfma32(a, pf[g], oacc[b]);
-                }
-            }
-        }
-        if (more) st.store(sK[buf ^ 1], sV[buf ^ 1], tid);
-        __syncthreads();
-    }
-
-    const float lt = wave_half_sum(l_run);
-    if (qrow < N) {
-        const float inv = 1.f / lt;
-        T* orow = O + head + (size_t)qrow * D;
-#pragma unroll
-        for (int b = 0; b < C::DB; ++b)
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                V4 w;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) w[i] = (T)(oacc[b][4 * r4 + i] * inv);
-                *reinterpret_cast<V4*>(orow + 32 * b + 8 * r4 + 4 * h) = w;
-            }
-        if (LSE != nullptr && h == 0) LSE[(size_t)bh * N + qrow] = (m_run + log2f(lt)) * kLn2;
-    }
+    w.finish(O + head, LSE == nullptr ? nullptr : LSE + (size_t)bh * N);
 }
 
 template <typename T, int D, bool CAUSAL>
 hipError_t launch_typed(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
                         int N, float scale, hipStream_t stream) {
-    using C = FwdTile<T, D>;
+    using C = FwdTile<D>;
     const int nqb = (N + C::BM - 1) / C::BM;
     const dim3 grid(BH * nqb), block(C::NT);
     hipLaunchKernelGGL((fwd_mfma_kernel<T, D, CAUSAL>), grid, block, 0, stream,

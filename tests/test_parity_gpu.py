@@ -11,10 +11,14 @@ Frobenius error ||gpu - oracle|| / ||oracle||):
   bf16 / fp16 forward  O max-abs <= 2e-2 and rel <= 1e-2
   bf16 / fp16 backward dQ, dK, dV max-abs <= 5e-2 and rel <= 1e-2
   fp8 forward          O rel <= 5e-2
-  LSE of the 16-bit and fp8 paths: max-abs <= 1e-3. The scores are exact
-  products of the rounded inputs accumulated in fp32 and the row sum uses the
-  unrounded fp32 probabilities, so LSE carries only fp32-level error
-  (~1e-5); 1e-3 leaves room for exp2/log2 approximations at N = 16K.
+  LSE of the 16-bit path: max-abs <= 1e-3. The scores are exact products of
+  the rounded inputs accumulated in fp32 and the row sum uses the unrounded
+  fp32 probabilities, so LSE carries only fp32-level error (~1e-5); 1e-3
+  leaves room for exp2/log2 approximations at N = 16K.
+  LSE of the fp8 path: |error| <= 1e-3 * max(1, |LSE|). With the x20 outliers
+  the scores reach |S| ~ 170, and the fp8 MFMA's internal accumulation was
+  measured to carry a relative error of ~2e-4 of |S| (absolute 0.03 at
+  S = 170), so the bound scales with the magnitude.
 Full-size workloads compare every element of sampled heads, or sampled query
 rows computed one by one by the oracle (each output row depends only on its
 own query row); properties that hold at any size are checked on all heads.
@@ -260,6 +264,10 @@ def test_closed_forms_gpu(gpu_lib):
 
 # ------------------------------------------------------------------ fp8 forward
 
+def lse_rel_err(got, ref):
+    return float(np.max(np.abs(got - ref) / np.maximum(1.0, np.abs(ref))))
+
+
 def fp8_case(fa, B, H, N, d, causal, seed):
     note(f"fwd fp8 B{B} H{H} N{N} d{d} causal={causal} seed={seed}")
     (q8, k8, v8), scales = inputs.draw_fp8(B, H, N, d, seed)
@@ -275,7 +283,7 @@ def test_fwd_fp8_small(gpu_lib, N, causal):
     o, lse, (q, k, v) = fp8_case(gpu_lib, 1, 2, N, 128, causal, 6000 + N)
     o_ref, l_ref = oracle.attention_forward(q, k, v, 128 ** -0.5, causal)
     assert rel_frob(o, o_ref) <= 5e-2
-    assert max_abs(lse, l_ref) <= 1e-3
+    assert lse_rel_err(lse, l_ref) <= 1e-3
 
 
 def test_fwd_fp8_workload(gpu_lib):
@@ -289,7 +297,7 @@ def test_fwd_fp8_workload(gpu_lib):
         o_ref, l_ref = oracle.attention_forward_rows(q[b, h], k[b, h], v[b, h], rows, d ** -0.5,
                                                      False)
         assert rel_frob(o[b, h, rows], o_ref) <= 5e-2, (b, h)
-        assert max_abs(lse[b, h, rows], l_ref) <= 1e-3, (b, h)
+        assert lse_rel_err(lse[b, h, rows], l_ref) <= 1e-3, (b, h)
 
 
 # ------------------------------------------------------------------ binding checks
