@@ -33,7 +33,8 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16/fp16 MFMA
 PEAK_FP8_TFLOPS = 5033.2    # MI355X dense fp8 MFMA
 KERNEL_SOURCES = {
     "fwd_mfma_kernel": "exact_io_aware_54_amd/csrc/fa_fwd.hip",
-    "bwd_main_kernel": "exact_io_aware_54_amd/csrc/fa_bwd.hip",
+    "bwd_dkdv_kernel": "exact_io_aware_54_amd/csrc/fa_bwd.hip",
+    "bwd_dq_kernel": "exact_io_aware_54_amd/csrc/fa_bwd.hip",
     "fwd_fp8_kernel": "exact_io_aware_54_amd/csrc/fa_fwd_fp8.hip",
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
@@ -145,16 +146,18 @@ def run_main(args):
     print(f"[bench] warmup {args.warmup}, timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     wall_ms, per = time_launches(fns, args.steps, args.warmup, torch)
-    fwd_ms, pre_ms, main_ms, conv_ms = per
+    fwd_ms, pre_ms, main_ms, conv_ms = per  # stage 2 = dK/dV pass, stage 3 = dQ pass
     f_fwd = counted_flops(B, H, N, d, causal)
     f_bwd = counted_flops(B, H, N, d, causal, backward=True)
     value = (f_fwd + f_bwd) / (wall_ms * 1e-3) / 1e12
     bwd_ms = pre_ms + main_ms + conv_ms
 
-    if main_ms >= fwd_ms:
-        kname, kflops, kms = "bwd_main_kernel", f_bwd, main_ms
-    else:
-        kname, kflops, kms = "fwd_mfma_kernel", f_fwd, fwd_ms
+    # Counted FLOPs per launch: the dK/dV pass does four of the backward's five
+    # counted contractions (S, dP, dV, dK), the dQ pass recomputes S and dP and
+    # adds dQ (three, of which only dQ is counted: 1/5 of the backward).
+    cands = [("fwd_mfma_kernel", f_fwd, fwd_ms), ("bwd_dkdv_kernel", 0.8 * f_bwd, main_ms),
+             ("bwd_dq_kernel", 0.2 * f_bwd, conv_ms)]
+    kname, kflops, kms = max(cands, key=lambda t: t[2])
     achieved = kflops / (kms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": kname, "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -181,8 +184,8 @@ def run_main(args):
         "cpu_baseline": cpu,
         "breakdown": {
             "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
-            "bwd_stage_ms": {"pre": round(pre_ms, 4), "main": round(main_ms, 4),
-                             "dq_convert": round(conv_ms, 4)},
+            "bwd_stage_ms": {"pre": round(pre_ms, 4), "dkdv": round(main_ms, 4),
+                             "dq": round(conv_ms, 4)},
             "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2),
             "bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2),
             "fwd_frac_peak": round(f_fwd / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),

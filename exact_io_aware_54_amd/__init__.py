@@ -162,7 +162,7 @@ def fa_bwd(q, k, v, o, lse, do, dq, dk, dv, workspace, scale, causal, stream=Non
 
 
 def fa_bwd_stage(stage, q, k, v, o, lse, do, dq, dk, dv, workspace, scale, causal, stream=None):
-    """Enqueue one of fa_bwd's three launches (1 preprocess, 2 main, 3 dQ convert)."""
+    """Enqueue one of fa_bwd's three launches (1 preprocess, 2 dK/dV, 3 dQ)."""
     import torch
     lib = load_library()
     B, H, N, d = q.shape

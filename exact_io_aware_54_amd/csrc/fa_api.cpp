@@ -83,7 +83,7 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, float q_descale, 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
     if (check_shape(B, H, N, d) != FA_OK) return 0;
     const size_t rows = (size_t)B * H * N;
-    return align256(rows * d * sizeof(float)) + align256(rows * sizeof(float));
+    return 2 * align256(rows * sizeof(float));  // D and LSE * log2(e), one float per row each
 }
 
 namespace {
@@ -99,11 +99,11 @@ int bwd_common(int dtype, const void* q, const void* k, const void* v, const voi
     if (workspace_bytes < fa_bwd_workspace_bytes(B, H, N, d)) return FA_ERR_WORKSPACE;
     if (((uintptr_t)workspace & 255) != 0) return FA_ERR_WORKSPACE;
     const size_t rows = (size_t)B * H * N;
-    float* dq_acc = static_cast<float*>(workspace);
-    float* delta = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                            align256(rows * d * sizeof(float)));
+    float* delta = static_cast<float*>(workspace);
+    float* lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                           align256(rows * sizeof(float)));
     return status_of(fa::launch_bwd(dtype, d, causal != 0, q, k, v, o, lse, dO, dq, dk, dv,
-                                    dq_acc, delta, B * H, N, scale, stages, stream));
+                                    delta, lse2, B * H, N, scale, stages, stream));
 }
 }  // namespace
 

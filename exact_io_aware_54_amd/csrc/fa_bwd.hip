@@ -10,18 +10,26 @@
 //   dQ  = scale dS K,  dK = scale dS^T Q.
 //
 // Three launches on the caller's stream:
-//  1. bwd_pre: D_i per row (fp32) and zeroing of the fp32 dQ accumulator.
-//  2. bwd_main: one workgroup per (batch*head, block of 128 keys); each of its
-//     four wavefronts keeps 32 keys' K and V rows in registers (as MFMA
-//     operands) and their dK, dV in MFMA accumulators for the whole kernel,
-//     and walks the query blocks of 64 rows (causal: only those at or below
-//     the diagonal). Per query block: S = Q K^T and dP = dO V^T (the key index
-//     across lanes, the query index in registers), P and dS in registers,
-//     dV^T += dO^T P and dK^T += Q^T dS with Q^T and dO^T read from LDS copies
-//     stored in the accumulator's row order. dS goes to LDS once, and the
-//     block's dQ = dS K is split across the four waves and added to the fp32
-//     accumulator with hardware float atomics.
-//  3. bwd_dq_convert: dQ accumulator -> dtype.
+//  1. bwd_pre: per row, D_i (fp32) and LSE_i * log2(e) into the workspace.
+//  2. bwd_dkdv: one workgroup per (batch*head, block of 128 keys). Each of
+//     its four wavefronts keeps its 32 keys' K and V rows in registers (B
+//     operands) and their dK^T, dV^T in MFMA accumulators for the whole
+//     kernel, and walks the query blocks of 64 rows (causal: from the
+//     diagonal on). Per block: S = Q K^T and dP = dO V^T with the key index
+//     across lanes and the query index in registers, P and dS in registers,
+//     then dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read straight
+//     out of the row-major Q / dO tiles by transposing LDS reads.
+//  3. bwd_dq: one workgroup per (batch*head, block of 128 queries), shaped
+//     like the forward: Q and dO rows of the wave's 32 queries stay in
+//     registers, K/V tiles stream through LDS; per tile S^T = K Q^T,
+//     dP^T = V dO^T, P^T and dS^T with the query across lanes, and
+//     dQ^T += K^T dS^T with K^T read transposed out of the K tile and dS^T
+//     used straight from registers.
+// dQ is computed by its own pass instead of float atomics from the dK/dV
+// pass: two more contractions (7 instead of 5) but no read-modify-write
+// traffic through memory, and every output is deterministic.
+// Q, dO, K and V tiles go HBM -> LDS with global_load_lds_dwordx4 into
+// double-buffered, XOR-swizzled (tile_swz) row-major buffers.
 
 #include "fa_device.h"
 #include "fa_launch.h"
@@ -29,37 +37,24 @@
 namespace fa {
 namespace {
 
-template <typename T, int D>
-struct BwdTile {
-    static constexpr int BN = 128;            // keys per workgroup (4 waves x 32)
-    static constexpr int BM = 64;             // queries per step
-    static constexpr int NT = 256;
-    static constexpr int QSTR = D + 8;        // row-layout Q / dO in LDS
-    static constexpr int TSTR = BM + 8;       // transposed Q^T / dO^T in LDS
-    static constexpr int SSTR = BN + 8;       // dS [BM][BN]
-    static constexpr int KTSTR = BN + 8;      // K^T [D][BN]
-    static constexpr int KS = D / 16;
-    static constexpr int DB = D / 32;
-    static constexpr int DCH = D / 8;
-    static constexpr int QG = BM * D / 8 / NT;   // rows per thread when staging Q / dO
-    static constexpr int KG = BN * D / 8 / NT;   // keys per thread when staging K^T
-    static constexpr int NSUB = (BM / 32) * DB;  // 32x32 dQ subtiles per step
-};
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-template <typename T, int N_>
-struct VecN;
-template <typename T>
-struct VecN<T, 2> { typedef __attribute__((__vector_size__(2 * sizeof(T)))) T type; };
-template <typename T>
-struct VecN<T, 4> { typedef __attribute__((__vector_size__(4 * sizeof(T)))) T type; };
-template <typename T>
-struct VecN<T, 8> { typedef __attribute__((__vector_size__(8 * sizeof(T)))) T type; };
+template <typename V8>
+__device__ __forceinline__ V8 tr_read8(const char* base, int off_lo, int off_hi) {
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off_lo));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off_hi));
+    const s16x4 w[2] = {lo, hi};
+    V8 a;
+    __builtin_memcpy(&a, w, sizeof(a));
+    return a;
+}
 
-// ---------------------------------------------------------------- 1. D and zeroing
+// ---------------------------------------------------------------- 1. D and LSE2
 template <typename T, int D>
 __global__ void __launch_bounds__(256)
-bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO, float* __restrict__ delta,
-               float* __restrict__ dq_acc, int rows) {
+bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO, const float* __restrict__ lse,
+               float* __restrict__ delta, float* __restrict__ lse2, int rows) {
     using V8 = typename Vec<T>::x8;
     constexpr int TPR = D / 8;  // threads per row
     const int gid = blockIdx.x * 256 + threadIdx.x;
@@ -70,151 +65,170 @@ bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO, float* __restr
         const V8 g = *reinterpret_cast<const V8*>(dO + (size_t)row * D + part * 8);
 #pragma unroll
         for (int i = 0; i < 8; ++i) s = fmaf((float)o[i], (float)g[i], s);
-        f32x4* z = reinterpret_cast<f32x4*>(dq_acc + (size_t)row * D + part * 8);
-        z[0] = f32x4{};
-        z[1] = f32x4{};
     }
 #pragma unroll
     for (int off = TPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, TPR);
-    if (row < rows && part == 0) delta[row] = s;
+    if (row < rows && part == 0) {
+        delta[row] = s;
+        lse2[row] = lse[row] * kLog2e;
+    }
 }
 
-// ---------------------------------------------------------------- 2. main
+// ---------------------------------------------------------------- 2. dK, dV
+template <int D>
+struct DkdvTile {
+    static constexpr int BN = 128;               // keys per workgroup (4 waves x 32)
+    static constexpr int BM = 64;                // queries per step
+    static constexpr int NT = 256;
+    static constexpr int ROWB = 2 * D;
+    static constexpr int TILEB = BM * ROWB;      // bytes of one Q (or dO) tile
+    static constexpr int NLOAD = TILEB / (NT * 16);
+    static constexpr int KS = D / 16;
+    static constexpr int DB = D / 32;
+};
+
 template <typename T, int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, 1)
-bwd_main_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-                const T* __restrict__ dO, const float* __restrict__ LSE,
-                const float* __restrict__ delta, float* __restrict__ dq_acc, T* __restrict__ dK,
-                T* __restrict__ dV, int BH, int N, int nkb, float scale, float c) {
-    using C = BwdTile<T, D>;
+struct DkdvWave {
+    using C = DkdvTile<D>;
     using V8 = typename Vec<T>::x8;
     using V4 = typename Vec<T>::x4;
-    using VG = typename VecN<T, C::QG>::type;
-    using VK = typename VecN<T, C::KG>::type;
-    __shared__ __attribute__((aligned(16))) T sQ[C::BM * C::QSTR];
-    __shared__ __attribute__((aligned(16))) T sdO[C::BM * C::QSTR];
-    __shared__ __attribute__((aligned(16))) T sQT[D * C::TSTR];
-    __shared__ __attribute__((aligned(16))) T sdOT[D * C::TSTR];
-    __shared__ __attribute__((aligned(16))) T sdS[C::BM * C::SSTR];
-    __shared__ __attribute__((aligned(16))) T sKT[D * C::KTSTR];
-    __shared__ float sL[C::BM];
-    __shared__ float sDel[C::BM];
 
-    const int L = xcd_remap(blockIdx.x, BH * nkb);
-    const int bh = L / nkb;
-    const int kb = L % nkb;  // causal: small kb has the most query blocks -> dispatched first
-    const size_t head = (size_t)bh * N * D;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l32 = lane & 31, h = lane >> 5;
-    const int kbase = kb * C::BN;
-    const int key0 = kbase + 32 * wave;  // first key of this wave
-    const int key = key0 + l32;          // key held by this lane (accumulator column)
+    const T* Qh;
+    const T* dOh;
+    const float* lse2h;
+    const float* delh;
+    int N, tid, lane, wave, l32, h, key0, key;
+    float c;
+    V8 kf[C::KS], vf[C::KS];         // B operands: K and V rows of this lane's key
+    int ld_row[C::NLOAD], ld_col[C::NLOAD];
+    int roff[2][C::KS];              // 16-byte row reads of Q / dO (query 32 qs + l32)
+    int toff[2][2][2][C::DB];        // transposing reads [qs][g2][half][b]
+    f32x16 dkacc[C::DB], dvacc[C::DB];  // dK^T, dV^T: head dim in registers, key = lane
 
-    // resident operands: K and V rows of this lane's key (B side of Q K^T and dO V^T)
-    V8 kf[C::KS], vf[C::KS];
-    if (key < N) {
-        const V8* ks = reinterpret_cast<const V8*>(K + head + (size_t)key * D + 8 * h);
-        const V8* vs = reinterpret_cast<const V8*>(V + head + (size_t)key * D + 8 * h);
+    __device__ __forceinline__ void init(const T* Qh_, const T* Kh, const T* Vh, const T* dOh_,
+                                         const float* lse2h_, const float* delh_, int N_, int kb,
+                                         float c_) {
+        Qh = Qh_;
+        dOh = dOh_;
+        lse2h = lse2h_;
+        delh = delh_;
+        N = N_;
+        c = c_;
+        tid = threadIdx.x;
+        lane = tid & 63;
+        wave = tid >> 6;
+        l32 = lane & 31;
+        h = lane >> 5;
+        key0 = kb * C::BN + 32 * wave;
+        key = key0 + l32;
+        const int kr = min(key, N - 1);
+        const V8* ks = reinterpret_cast<const V8*>(Kh + (size_t)kr * D + 8 * h);
+        const V8* vs = reinterpret_cast<const V8*>(Vh + (size_t)kr * D + 8 * h);
 #pragma unroll
         for (int s = 0; s < C::KS; ++s) {
             kf[s] = ks[2 * s];
             vf[s] = vs[2 * s];
         }
-    } else {
 #pragma unroll
-        for (int s = 0; s < C::KS; ++s) {
-            kf[s] = V8{};
-            vf[s] = V8{};
-        }
-    }
-    // K^T of the whole key block into LDS (B side of dQ = dS K), natural key order
-    {
-        const int cc = tid % C::DCH, g = tid / C::DCH;
-        V8 kr[C::KG];
-#pragma unroll
-        for (int i = 0; i < C::KG; ++i) {
-            const int kk = kbase + g * C::KG + i;
-            kr[i] = kk < N ? *reinterpret_cast<const V8*>(K + head + (size_t)kk * D + cc * 8) : V8{};
+        for (int i = 0; i < C::NLOAD; ++i) {
+            const int byte = i * (C::NT * 16) + tid * 16;
+            const int r = byte / C::ROWB, p = (byte % C::ROWB) / 16;
+            ld_row[i] = r;
+            ld_col[i] = (p ^ tile_swz<D>(r)) * 8;
         }
 #pragma unroll
-        for (int dd = 0; dd < 8; ++dd) {
-            VK w;
+        for (int qs = 0; qs < 2; ++qs)
 #pragma unroll
-            for (int i = 0; i < C::KG; ++i) w[i] = kr[i][dd];
-            *reinterpret_cast<VK*>(sKT + (cc * 8 + dd) * C::KTSTR + g * C::KG) = w;
+            for (int s = 0; s < C::KS; ++s) roff[qs][s] = tile_off<D>(32 * qs + l32, 16 * s + 8 * h);
+        // transposing reads: this lane supplies row 32 qs + 16 g2 + 8 half + 4 h +
+        // (lane % 16) / 4 and head dims 32 b + 16 ((lane / 16) % 2) + 4 (lane % 4);
+        // it receives head dim 32 b + lane % 32 at queries 32 qs + 16 g2 + 8 half
+        // + 4 h + 0..3, the order of registers 8 g2 + 4 half + 0..3 of the
+        // score accumulator of query subtile qs.
+        const int src_r = 4 * h + (lane & 15) / 4;
+        const int src_d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+            for (int g2 = 0; g2 < 2; ++g2)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                    for (int b = 0; b < C::DB; ++b)
+                        toff[qs][g2][hf][b] =
+                            tile_off<D>(32 * qs + 16 * g2 + 8 * hf + src_r, 32 * b + src_d);
+#pragma unroll
+        for (int b = 0; b < C::DB; ++b) {
+            dkacc[b] = f32x16{};
+            dvacc[b] = f32x16{};
         }
     }
 
-    f32x16 dvacc[C::DB], dkacc[C::DB];
+    // Q and dO rows [qbase, qbase + BM) and their LSE2 / D into one buffer set.
+    __device__ __forceinline__ void issue(int qbase, char* sQd, char* sGd, float* sLd,
+                                          float* sDd) const {
 #pragma unroll
-    for (int b = 0; b < C::DB; ++b) {
-        dvacc[b] = f32x16{};
-        dkacc[b] = f32x16{};
+        for (int i = 0; i < C::NLOAD; ++i) {
+            const size_t row = (size_t)min(qbase + ld_row[i], N - 1) * D;
+            const int o = i * (C::NT * 16) + wave * 1024;
+            __builtin_amdgcn_global_load_lds(Qh + row + ld_col[i], sQd + o, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(dOh + row + ld_col[i], sGd + o, 16, 0, 0);
+        }
+        const int r = min(qbase + lane, N - 1);
+        if (wave == 0) __builtin_amdgcn_global_load_lds(lse2h + r, sLd, 4, 0, 0);
+        if (wave == 1) __builtin_amdgcn_global_load_lds(delh + r, sDd, 4, 0, 0);
     }
 
-    const int nqb = (N + C::BM - 1) / C::BM;
-    const int i0 = CAUSAL ? kbase / C::BM : 0;
-    for (int ib = i0; ib < nqb; ++ib) {
+    __device__ __forceinline__ void step(int ib, int nqb, const char* sQ, const char* sG,
+                                         const float* sL, const float* sD, char* nQ, char* nG,
+                                         float* nL, float* nD) {
         const int qbase = ib * C::BM;
-        __syncthreads();  // previous step's LDS readers are done
-        {
-            // stage Q and dO rows [qbase, qbase + BM): row layout and transposed layout
-            const int cc = tid % C::DCH, g = tid / C::DCH;
-            V8 qr[C::QG], gr[C::QG];
-#pragma unroll
-            for (int i = 0; i < C::QG; ++i) {
-                const int r = g * C::QG + i, row = qbase + r;
-                if (row < N) {
-                    qr[i] = *reinterpret_cast<const V8*>(Q + head + (size_t)row * D + cc * 8);
-                    gr[i] = *reinterpret_cast<const V8*>(dO + head + (size_t)row * D + cc * 8);
-                } else {
-                    qr[i] = V8{};
-                    gr[i] = V8{};
-                }
-                *reinterpret_cast<V8*>(sQ + r * C::QSTR + cc * 8) = qr[i];
-                *reinterpret_cast<V8*>(sdO + r * C::QSTR + cc * 8) = gr[i];
-            }
-            const int r0 = g * C::QG;
-            const int pos = (r0 & ~15) + acc_kperm16(r0 & 15);
-#pragma unroll
-            for (int dd = 0; dd < 8; ++dd) {
-                VG wq, wg;
-#pragma unroll
-                for (int i = 0; i < C::QG; ++i) {
-                    wq[i] = qr[i][dd];
-                    wg[i] = gr[i][dd];
-                }
-                *reinterpret_cast<VG*>(sQT + (cc * 8 + dd) * C::TSTR + pos) = wq;
-                *reinterpret_cast<VG*>(sdOT + (cc * 8 + dd) * C::TSTR + pos) = wg;
-            }
-            if (tid < C::BM) {
-                const int row = qbase + tid;
-                const size_t ri = (size_t)bh * N + row;
-                sL[tid] = row < N ? LSE[ri] * kLog2e : INFINITY;  // +inf -> P = 0 for padding rows
-                sDel[tid] = row < N ? delta[ri] : 0.f;
-            }
-        }
+        __builtin_amdgcn_s_waitcnt(kVmcntZero);
         __syncthreads();
+        if (ib + 1 < nqb) issue(qbase + C::BM, nQ, nG, nL, nD);
+        if (CAUSAL && key0 > qbase + C::BM - 1) return;  // every query of the block precedes every key
 
-        const bool need_mask = (key0 + 31 >= N) || (CAUSAL && key0 + 31 > qbase);
 #pragma unroll
-        for (int qs = 0; qs < C::BM / 32; ++qs) {
+        for (int qs = 0; qs < 2; ++qs) {
             f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
             for (int s = 0; s < C::KS; ++s) {
-                const V8 aq = *reinterpret_cast<const V8*>(sQ + (32 * qs + l32) * C::QSTR + 16 * s + 8 * h);
-                const V8 ag = *reinterpret_cast<const V8*>(sdO + (32 * qs + l32) * C::QSTR + 16 * s + 8 * h);
+                const V8 aq = *reinterpret_cast<const V8*>(sQ + roff[qs][s]);
+                const V8 ag = *reinterpret_cast<const V8*>(sG + roff[qs][s]);
                 sacc = mfma32(aq, kf[s], sacc);
                 pacc = mfma32(ag, vf[s], pacc);
             }
-            // sacc / pacc: lane = key, register r = query 32 qs + acc_row(r, h)
+            // lane = key, register r = query 32 qs + acc_row(r, h) of the block
+            float lq[16], dq[16];
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const f32x4 a = *reinterpret_cast<const f32x4*>(sL + 32 * qs + 8 * r4 + 4 * h);
+                const f32x4 b = *reinterpret_cast<const f32x4*>(sD + 32 * qs + 8 * r4 + 4 * h);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    lq[4 * r4 + i] = a[i];
+                    dq[4 * r4 + i] = b[i];
+                }
+            }
+            const int qb0 = qbase + 32 * qs;
+            const bool need_mask = key0 + 31 >= N || qb0 + 31 >= N || (CAUSAL && key0 + 31 > qb0);
+            if (need_mask) {
+                // query qb0 + 8 (r / 4) + (r % 4) + 4 h is valid iff < N and (causal) >= key
+                const int lo = key - qb0 - 4 * h;   // const(r) >= lo when causal-visible
+                const int hi = N - qb0 - 4 * h;     // const(r) < hi when query < N
+                const bool kvalid = key < N;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int cr = 8 * (r >> 2) + (r & 3);
+                    const bool vis = kvalid && cr < hi && (!CAUSAL || cr >= lo);
+                    if (!vis) lq[r] = INFINITY;  // P = 2^(s c - inf) = 0
+                }
+            }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int qi = 32 * qs + acc_row(r, h);
-                float p = fast_exp2(fmaf(sacc[r], c, -sL[qi]));
-                if (need_mask && (key >= N || (CAUSAL && key > qbase + qi))) p = 0.f;
+                const float p = fast_exp2(fmaf(sacc[r], c, -lq[r]));
                 sacc[r] = p;
-                pacc[r] = p * (pacc[r] - sDel[qi]);
+                pacc[r] = p * (pacc[r] - dq[r]);
             }
             V8 pf[2], sf[2];
             pf[0] = pack8<T>(sacc, 0);
@@ -225,44 +239,18 @@ bwd_main_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
             for (int g2 = 0; g2 < 2; ++g2)
 #pragma unroll
                 for (int b = 0; b < C::DB; ++b) {
-                    const int off = (32 * b + l32) * C::TSTR + 32 * qs + 16 * g2 + 8 * h;
-                    const V8 at = *reinterpret_cast<const V8*>(sdOT + off);
-                    const V8 aq = *reinterpret_cast<const V8*>(sQT + off);
+                    const V8 at = tr_read8<V8>(sG, toff[qs][g2][0][b], toff[qs][g2][1][b]);
                     dvacc[b] = mfma32(at, pf[g2], dvacc[b]);
+                    const V8 aq = tr_read8<V8>(sQ, toff[qs][g2][0][b], toff[qs][g2][1][b]);
                     dkacc[b] = mfma32(aq, sf[g2], dkacc[b]);
                 }
-            // dS [q][key] for the dQ product
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                sdS[(32 * qs + acc_row(r, h)) * C::SSTR + 32 * wave + l32] = (T)pacc[r];
-        }
-        __syncthreads();
-
-        // dQ[qbase.., :] += scale * dS K over this block's 128 keys
-#pragma unroll
-        for (int u = 0; u < C::NSUB / 4; ++u) {
-            const int t = wave + 4 * u;
-            const int qs = t / C::DB, b = t % C::DB;
-            f32x16 acc = f32x16{};
-#pragma unroll
-            for (int s = 0; s < C::BN / 16; ++s) {
-                const V8 a = *reinterpret_cast<const V8*>(sdS + (32 * qs + l32) * C::SSTR + 16 * s + 8 * h);
-                const V8 bb = *reinterpret_cast<const V8*>(sKT + (32 * b + l32) * C::KTSTR + 16 * s + 8 * h);
-                acc = mfma32(a, bb, acc);
-            }
-            // acc: lane = head dim 32 b + l32, register r = query 32 qs + acc_row(r, h)
-            float* dst = dq_acc + head + 32 * b + l32;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = qbase + 32 * qs + acc_row(r, h);
-                if (row < N) unsafeAtomicAdd(dst + (size_t)row * D, acc[r] * scale);
-            }
         }
     }
 
-    if (key < N) {
-        T* dkr = dK + head + (size_t)key * D;
-        T* dvr = dV + head + (size_t)key * D;
+    __device__ __forceinline__ void finish(T* dKh, T* dVh, float scale) {
+        if (key >= N) return;
+        T* dkr = dKh + (size_t)key * D;
+        T* dvr = dVh + (size_t)key * D;
 #pragma unroll
         for (int b = 0; b < C::DB; ++b)
 #pragma unroll
@@ -277,54 +265,261 @@ bwd_main_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
                 *reinterpret_cast<V4*>(dvr + 32 * b + 8 * r4 + 4 * h) = wv;
             }
     }
+};
+
+template <typename T, int D, bool CAUSAL>
+__global__ void __launch_bounds__(256, 1)
+bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+                const T* __restrict__ dO, const float* __restrict__ lse2,
+                const float* __restrict__ delta, T* __restrict__ dK, T* __restrict__ dV, int BH,
+                int N, int nkb, float scale, float c) {
+    using C = DkdvTile<D>;
+    __shared__ __attribute__((aligned(1024))) char sQ0[C::TILEB];
+    __shared__ __attribute__((aligned(1024))) char sQ1[C::TILEB];
+    __shared__ __attribute__((aligned(1024))) char sG0[C::TILEB];
+    __shared__ __attribute__((aligned(1024))) char sG1[C::TILEB];
+    __shared__ __attribute__((aligned(256))) float sL0[C::BM];
+    __shared__ __attribute__((aligned(256))) float sL1[C::BM];
+    __shared__ __attribute__((aligned(256))) float sD0[C::BM];
+    __shared__ __attribute__((aligned(256))) float sD1[C::BM];
+
+    const int L = xcd_remap(blockIdx.x, BH * nkb);
+    const int bh = L / nkb;
+    const int kb = L % nkb;  // causal: small kb has the most query blocks -> dispatched first
+    const size_t head = (size_t)bh * N * D;
+    const size_t rowbase = (size_t)bh * N;
+
+    DkdvWave<T, D, CAUSAL> w;
+    w.init(Q + head, K + head, V + head, dO + head, lse2 + rowbase, delta + rowbase, N, kb, c);
+    const int nqb = (N + C::BM - 1) / C::BM;
+    const int i0 = CAUSAL ? (kb * C::BN) / C::BM : 0;
+    w.issue(i0 * C::BM, sQ0, sG0, sL0, sD0);
+    for (int ib = i0; ib < nqb; ib += 2) {
+        w.step(ib, nqb, sQ0, sG0, sL0, sD0, sQ1, sG1, sL1, sD1);
+        if (ib + 1 < nqb) w.step(ib + 1, nqb, sQ1, sG1, sL1, sD1, sQ0, sG0, sL0, sD0);
+    }
+    w.finish(dK + head, dV + head, scale);
 }
 
-// ---------------------------------------------------------------- 3. dQ convert
-template <typename T>
-__global__ void __launch_bounds__(256)
-bwd_dq_convert_kernel(const float* __restrict__ acc, T* __restrict__ dq, size_t n8) {
+// ---------------------------------------------------------------- 3. dQ
+template <int D>
+struct DqTile {
+    static constexpr int BM = 128;               // queries per workgroup (4 waves x 32)
+    static constexpr int BN = 64;                // keys per tile
+    static constexpr int NT = 256;
+    static constexpr int ROWB = 2 * D;
+    static constexpr int TILEB = BN * ROWB;
+    static constexpr int NLOAD = TILEB / (NT * 16);
+    static constexpr int KS = D / 16;
+    static constexpr int DB = D / 32;
+};
+
+template <typename T, int D, bool CAUSAL>
+struct DqWave {
+    using C = DqTile<D>;
     using V8 = typename Vec<T>::x8;
-    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n8) return;
-    const f32x4* src = reinterpret_cast<const f32x4*>(acc) + 2 * i;
-    const f32x4 a = src[0], b = src[1];
-    V8 w;
+    using V4 = typename Vec<T>::x4;
+
+    const T* Kh;
+    const T* Vh;
+    int N, nkt, tid, lane, wave, l32, h, q0, qrow;
+    float c, lse2, del;
+    V8 qf[C::KS], gf[C::KS];        // B operands: Q and dO rows of this lane's query
+    int ld_row[C::NLOAD], ld_col[C::NLOAD];
+    int roff[2][C::KS];             // 16-byte row reads of K / V (key 32 c2 + l32)
+    int toff[4][2][C::DB];          // transposing reads of K [g][half][b]
+    f32x16 dqacc[C::DB];            // dQ^T: head dim in registers, query = lane
+
+    __device__ __forceinline__ void init(const T* Qh, const T* Kh_, const T* Vh_, const T* dOh,
+                                         const float* lse2h, const float* delh, int N_, int qb,
+                                         float c_) {
+        Kh = Kh_;
+        Vh = Vh_;
+        N = N_;
+        c = c_;
+        tid = threadIdx.x;
+        lane = tid & 63;
+        wave = tid >> 6;
+        l32 = lane & 31;
+        h = lane >> 5;
+        q0 = qb * C::BM + 32 * wave;
+        qrow = q0 + l32;
+        const int qr = min(qrow, N - 1);
+        const V8* qs = reinterpret_cast<const V8*>(Qh + (size_t)qr * D + 8 * h);
+        const V8* gs = reinterpret_cast<const V8*>(dOh + (size_t)qr * D + 8 * h);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        w[j] = (T)a[j];
-        w[j + 4] = (T)b[j];
+        for (int s = 0; s < C::KS; ++s) {
+            qf[s] = qs[2 * s];
+            gf[s] = gs[2 * s];
+        }
+        lse2 = lse2h[qr];
+        del = delh[qr];
+        const int q_last = min(N, (qb + 1) * C::BM) - 1;
+        nkt = CAUSAL ? (q_last / C::BN + 1) : (N + C::BN - 1) / C::BN;
+#pragma unroll
+        for (int i = 0; i < C::NLOAD; ++i) {
+            const int byte = i * (C::NT * 16) + tid * 16;
+            const int r = byte / C::ROWB, p = (byte % C::ROWB) / 16;
+            ld_row[i] = r;
+            ld_col[i] = (p ^ tile_swz<D>(r)) * 8;
+        }
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+            for (int s = 0; s < C::KS; ++s) roff[c2][s] = tile_off<D>(32 * c2 + l32, 16 * s + 8 * h);
+        // transposing reads of K: this lane supplies key 16 g + 8 half + 4 h +
+        // (lane % 16) / 4, head dims 32 b + 16 ((lane / 16) % 2) + 4 (lane % 4);
+        // it receives head dim 32 b + lane % 32 at keys 16 g + 8 half + 4 h + 0..3,
+        // the key order of registers 8 (g % 2) + 4 half + 0..3 of dS^T subtile g / 2.
+        const int src_r = 4 * h + (lane & 15) / 4;
+        const int src_d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int b = 0; b < C::DB; ++b)
+                    toff[g][hf][b] = tile_off<D>(16 * g + 8 * hf + src_r, 32 * b + src_d);
+#pragma unroll
+        for (int b = 0; b < C::DB; ++b) dqacc[b] = f32x16{};
     }
-    reinterpret_cast<V8*>(dq)[i] = w;
+
+    __device__ __forceinline__ void issue(int kbase, char* sKd, char* sVd) const {
+#pragma unroll
+        for (int i = 0; i < C::NLOAD; ++i) {
+            const size_t row = (size_t)min(kbase + ld_row[i], N - 1) * D;
+            const int o = i * (C::NT * 16) + wave * 1024;
+            __builtin_amdgcn_global_load_lds(Kh + row + ld_col[i], sKd + o, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(Vh + row + ld_col[i], sVd + o, 16, 0, 0);
+        }
+    }
+
+    __device__ __forceinline__ void step(int kt, const char* kb, const char* vb, char* kn,
+                                         char* vn) {
+        const int kbase = kt * C::BN;
+        __builtin_amdgcn_s_waitcnt(kVmcntZero);
+        __syncthreads();
+        if (kt + 1 < nkt) issue(kbase + C::BN, kn, vn);
+        if (CAUSAL && kbase > q0 + 31) return;
+
+        f32x16 s[2], dp[2];
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+            s[c2] = f32x16{};
+            dp[c2] = f32x16{};
+        }
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) {
+                const V8 ak = *reinterpret_cast<const V8*>(kb + roff[c2][ks]);
+                const V8 av = *reinterpret_cast<const V8*>(vb + roff[c2][ks]);
+                s[c2] = mfma32(ak, qf[ks], s[c2]);
+                dp[c2] = mfma32(av, gf[ks], dp[c2]);
+            }
+        const bool need_mask = (kbase + C::BN > N) || (CAUSAL && kbase + C::BN - 1 > q0);
+        if (need_mask) {
+            const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - kbase - 4 * h;
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (32 * c2 + 8 * (r >> 2) + (r & 3) > lim) s[c2][r] = -INFINITY;
+        }
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = fast_exp2(fmaf(s[c2][r], c, -lse2));
+                dp[c2][r] = p * (dp[c2][r] - del);
+            }
+        V8 sf[4];
+        sf[0] = pack8<T>(dp[0], 0);
+        sf[1] = pack8<T>(dp[0], 8);
+        sf[2] = pack8<T>(dp[1], 0);
+        sf[3] = pack8<T>(dp[1], 8);
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int b = 0; b < C::DB; ++b) {
+                const V8 a = tr_read8<V8>(kb, toff[g][0][b], toff[g][1][b]);
+                dqacc[b] = mfma32(a, sf[g], dqacc[b]);
+            }
+    }
+
+    __device__ __forceinline__ void finish(T* dQh, float scale) {
+        if (qrow >= N) return;
+        T* dst = dQh + (size_t)qrow * D;
+#pragma unroll
+        for (int b = 0; b < C::DB; ++b)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                V4 w;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w[i] = (T)(dqacc[b][4 * r4 + i] * scale);
+                *reinterpret_cast<V4*>(dst + 32 * b + 8 * r4 + 4 * h) = w;
+            }
+    }
+};
+
+template <typename T, int D, bool CAUSAL>
+__global__ void __launch_bounds__(256, 2)
+bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+              const T* __restrict__ dO, const float* __restrict__ lse2,
+              const float* __restrict__ delta, T* __restrict__ dQ, int BH, int N, int nqb,
+              float scale, float c) {
+    using C = DqTile<D>;
+    __shared__ __attribute__((aligned(1024))) char sK0[C::TILEB];
+    __shared__ __attribute__((aligned(1024))) char sK1[C::TILEB];
+    __shared__ __attribute__((aligned(1024))) char sV0[C::TILEB];
+    __shared__ __attribute__((aligned(1024))) char sV1[C::TILEB];
+
+    const int L = xcd_remap(blockIdx.x, BH * nqb);
+    const int bh = L / nqb;
+    const int qb = CAUSAL ? (nqb - 1 - L % nqb) : (L % nqb);
+    const size_t head = (size_t)bh * N * D;
+    const size_t rowbase = (size_t)bh * N;
+
+    DqWave<T, D, CAUSAL> w;
+    w.init(Q + head, K + head, V + head, dO + head, lse2 + rowbase, delta + rowbase, N, qb, c);
+    w.issue(0, sK0, sV0);
+    for (int kt = 0; kt < w.nkt; kt += 2) {
+        w.step(kt, sK0, sV0, sK1, sV1);
+        if (kt + 1 < w.nkt) w.step(kt + 1, sK1, sV1, sK0, sV0);
+    }
+    w.finish(dQ + head, scale);
 }
 
 template <typename T, int D, bool CAUSAL>
 hipError_t launch_typed(const void* q, const void* k, const void* v, const void* o,
                         const float* lse, const void* dO, void* dq, void* dk, void* dv,
-                        float* dq_acc, float* delta, int BH, int N, float scale, int stages,
+                        float* delta, float* lse2, int BH, int N, float scale, int stages,
                         hipStream_t stream) {
-    using C = BwdTile<T, D>;
     const int rows = BH * N;
+    const float c = scale * kLog2e;
+    auto tq = static_cast<const T*>(q);
+    auto tk = static_cast<const T*>(k);
+    auto tv = static_cast<const T*>(v);
+    auto tdo = static_cast<const T*>(dO);
     hipError_t e = hipSuccess;
     if (stages & 1) {
-        const int pre_threads = rows * (D / 8);
-        hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((pre_threads + 255) / 256), dim3(256), 0,
-                           stream, static_cast<const T*>(o), static_cast<const T*>(dO), delta,
-                           dq_acc, rows);
+        const int threads = rows * (D / 8);
+        hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((threads + 255) / 256), dim3(256), 0,
+                           stream, static_cast<const T*>(o), tdo, lse, delta, lse2, rows);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (stages & 2) {
-        const int nkb = (N + C::BN - 1) / C::BN;
-        hipLaunchKernelGGL((bwd_main_kernel<T, D, CAUSAL>), dim3(BH * nkb), dim3(C::NT), 0,
-                           stream, static_cast<const T*>(q), static_cast<const T*>(k),
-                           static_cast<const T*>(v), static_cast<const T*>(dO), lse, delta,
-                           dq_acc, static_cast<T*>(dk), static_cast<T*>(dv), BH, N, nkb, scale,
-                           scale * kLog2e);
+        const int nkb = (N + DkdvTile<D>::BN - 1) / DkdvTile<D>::BN;
+        hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3(BH * nkb), dim3(256), 0, stream,
+                           tq, tk, tv, tdo, lse2, delta, static_cast<T*>(dk), static_cast<T*>(dv),
+                           BH, N, nkb, scale, c);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (stages & 4) {
-        const size_t n8 = (size_t)rows * D / 8;
-        hipLaunchKernelGGL((bwd_dq_convert_kernel<T>), dim3((unsigned)((n8 + 255) / 256)),
-                           dim3(256), 0, stream, dq_acc, static_cast<T*>(dq), n8);
+        const int nqb = (N + DqTile<D>::BM - 1) / DqTile<D>::BM;
+        hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3(BH * nqb), dim3(256), 0, stream,
+                           tq, tk, tv, tdo, lse2, delta, static_cast<T*>(dq), BH, N, nqb, scale,
+                           c);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return e;
@@ -333,29 +528,29 @@ hipError_t launch_typed(const void* q, const void* k, const void* v, const void*
 template <typename T>
 hipError_t launch_d(int d, bool causal, const void* q, const void* k, const void* v,
                     const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv,
-                    float* dq_acc, float* delta, int BH, int N, float scale, int stages,
+                    float* delta, float* lse2, int BH, int N, float scale, int stages,
                     hipStream_t stream) {
     if (d == 64)
-        return causal ? launch_typed<T, 64, true>(q, k, v, o, lse, dO, dq, dk, dv, dq_acc, delta,
+        return causal ? launch_typed<T, 64, true>(q, k, v, o, lse, dO, dq, dk, dv, delta, lse2,
                                                   BH, N, scale, stages, stream)
-                      : launch_typed<T, 64, false>(q, k, v, o, lse, dO, dq, dk, dv, dq_acc,
-                                                   delta, BH, N, scale, stages, stream);
-    return causal ? launch_typed<T, 128, true>(q, k, v, o, lse, dO, dq, dk, dv, dq_acc, delta, BH,
+                      : launch_typed<T, 64, false>(q, k, v, o, lse, dO, dq, dk, dv, delta, lse2,
+                                                   BH, N, scale, stages, stream);
+    return causal ? launch_typed<T, 128, true>(q, k, v, o, lse, dO, dq, dk, dv, delta, lse2, BH,
                                                N, scale, stages, stream)
-                  : launch_typed<T, 128, false>(q, k, v, o, lse, dO, dq, dk, dv, dq_acc, delta,
-                                                BH, N, scale, stages, stream);
+                  : launch_typed<T, 128, false>(q, k, v, o, lse, dO, dq, dk, dv, delta, lse2, BH,
+                                                N, scale, stages, stream);
 }
 
 }  // namespace
 
 hipError_t launch_bwd(int dtype, int d, bool causal, const void* q, const void* k, const void* v,
                       const void* o, const float* lse, const void* dO, void* dq, void* dk,
-                      void* dv, float* dq_acc, float* delta, int BH, int N, float scale,
+                      void* dv, float* delta, float* lse2, int BH, int N, float scale,
                       int stages, hipStream_t stream) {
     if (dtype == 2)
-        return launch_d<__bf16>(d, causal, q, k, v, o, lse, dO, dq, dk, dv, dq_acc, delta, BH, N,
+        return launch_d<__bf16>(d, causal, q, k, v, o, lse, dO, dq, dk, dv, delta, lse2, BH, N,
                                 scale, stages, stream);
-    return launch_d<_Float16>(d, causal, q, k, v, o, lse, dO, dq, dk, dv, dq_acc, delta, BH, N,
+    return launch_d<_Float16>(d, causal, q, k, v, o, lse, dO, dq, dk, dv, delta, lse2, BH, N,
                               scale, stages, stream);
 }
 

@@ -90,4 +90,33 @@ __device__ __forceinline__ int acc_kperm16(int kk) {
     return pos4 * 4 + i;
 }
 
+// LDS layout of a row-major tile of 16-bit rows with D elements (D = 64 or
+// 128) staged by global_load_lds: 16-byte chunk c of row r is stored at chunk
+// position c ^ tile_swz<D>(r). The XOR pattern is chosen so that both read
+// patterns used on these tiles touch every bank exactly once per pass:
+//  * 16-byte row reads: 16 consecutive rows, one chunk each;
+//  * ds_read_b64_tr_b16: 4 consecutive rows (first one a multiple of 4),
+//    4 consecutive chunks each (chunk index a multiple of 4 first).
+// D = 128 (one row per 256 bytes of banks): swap the two 2-bit halves of r%16.
+// D = 64 (two rows per 256 bytes): g = (r/2)%8, rotate its 3 bits right by 1.
+template <int D>
+__device__ __forceinline__ int tile_swz(int r) {
+    static_assert(D == 64 || D == 128, "head dim 64 or 128");
+    if constexpr (D == 128) {
+        return ((r & 3) << 2) | ((r >> 2) & 3);
+    } else {
+        const int g = (r >> 1) & 7;
+        return ((g & 1) << 2) | (g >> 1);
+    }
+}
+
+// Byte offset, inside such a tile, of element d (a multiple of 4 when used
+// for transposing reads, of 8 for 16-byte reads) of row r.
+template <int D>
+__device__ __forceinline__ int tile_off(int r, int d) {
+    return r * (2 * D) + 16 * ((d >> 3) ^ tile_swz<D>(r)) + 2 * (d & 7);
+}
+
+constexpr int kVmcntZero = 0x0F70;  // s_waitcnt vmcnt(0), expcnt/lgkmcnt untouched
+
 }  // namespace fa

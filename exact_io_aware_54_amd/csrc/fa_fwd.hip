@@ -22,8 +22,8 @@
 //  * K and V tiles go HBM -> LDS with global_load_lds_dwordx4 (no VGPR
 //    staging, no VALU), double-buffered: the next tile's loads are issued
 //    before the current tile is computed. Both are stored row-major with an
-//    XOR swizzle of the 16-byte chunks so that the MFMA operand reads are
-//    free of bank conflicts. K is read as 16-byte rows; V^T is read with
+//    XOR swizzle of the 16-byte chunks (tile_swz) so that the MFMA operand
+//    reads are free of bank conflicts. K is read as 16-byte rows; V^T with
 //    ds_read_b64_tr_b16, which transposes 4x4 blocks of 16-bit elements
 //    across lanes on the way out of LDS.
 //  * Softmax works in base 2: p = 2^(s * scale * log2 e - m) via v_exp_f32.
@@ -51,31 +51,13 @@ struct FwdTile {
     static constexpr int BN = 64;                  // keys per K/V tile
     static constexpr int NT = 256;                 // threads per workgroup
     static constexpr int ROWB = D * 2;             // bytes per K/V row
-    static constexpr int CH = D / 8;               // 16-byte chunks per row
-    static constexpr int RPB = 256 / ROWB;         // rows per 256 bytes (one pass of banks)
     static constexpr int TILEB = BN * ROWB;        // bytes per K (or V) tile
     static constexpr int NLOAD = TILEB / (NT * 16);  // direct loads per thread per tile
     static constexpr int KS = D / 16;              // MFMA k-steps over the head dim
     static constexpr int DB = D / 32;              // 32-row blocks of O^T
 };
 
-// Chunk swizzles (chunk index within a row -> stored position).
-// K rows are read 16 consecutive rows x one chunk at a time: XOR with the row.
-template <int D>
-__device__ __forceinline__ int kswz(int r) {
-    using C = FwdTile<D>;
-    return (r / C::RPB) % C::CH;
-}
-// V rows are read 4 rows x 4 chunks at a time (transposing reads): spread
-// the four rows over the four 64-byte quarters of the banks.
-template <int D>
-__device__ __forceinline__ int vswz(int r) {
-    using C = FwdTile<D>;
-    return 4 * ((r / C::RPB) % (C::CH / 4));
-}
-
 constexpr float kRescaleThreshold = 8.f;  // log2 units: refresh m when it grows by > 2^8
-constexpr int kVmcntZero = 0x0F70;        // s_waitcnt vmcnt(0), expcnt/lgkmcnt untouched
 
 // Per-wavefront state of the forward kernel and its steps.
 template <typename T, int D, bool CAUSAL>
@@ -89,7 +71,7 @@ struct FwdWave {
     int N, nkt, tid, wave, lane, h, l32, q0, qrow;
     float c;
     V8 qf[C::KS];               // B operand of S^T = K Q^T (d = 16 s + 8 h + j)
-    int ld_row[C::NLOAD], ld_kcol[C::NLOAD], ld_vcol[C::NLOAD];
+    int ld_row[C::NLOAD], ld_col[C::NLOAD];
     int koff[2][C::KS];         // LDS byte offsets of the K operand reads
     int voff[4][2][C::DB];      // LDS byte offsets of the V^T transposing reads
     float m_run, l_run;         // running (reference) max of s * c and this lane's sum
@@ -116,23 +98,21 @@ struct FwdWave {
 
         // Direct-load map: load i of this thread fills LDS bytes [i*4096 +
         // tid*16, +16) of a tile, i.e. row r, stored chunk position p; it
-        // fetches global chunk p ^ swz(r) of that row (rows past N re-read row
-        // N-1; their scores are masked).
+        // fetches global chunk p ^ tile_swz(r) of that row (rows past N re-read
+        // row N-1; their scores are masked).
 #pragma unroll
         for (int i = 0; i < C::NLOAD; ++i) {
             const int byte = i * (C::NT * 16) + tid * 16;
             const int r = byte / C::ROWB, p = (byte % C::ROWB) / 16;
             ld_row[i] = r;
-            ld_kcol[i] = (p ^ kswz<D>(r)) * 8;
-            ld_vcol[i] = (p ^ vswz<D>(r)) * 8;
+            ld_col[i] = (p ^ tile_swz<D>(r)) * 8;
         }
         // K (A side of S^T): key 32 c2 + l32, chunk 2 s + h.
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
             for (int s = 0; s < C::KS; ++s) {
-                const int r = 32 * c2 + l32;
-                koff[c2][s] = r * C::ROWB + 16 * ((2 * s + h) ^ kswz<D>(r));
+                koff[c2][s] = tile_off<D>(32 * c2 + l32, 16 * s + 8 * h);
             }
         // V^T (A side of O^T = V^T P^T) via transposing reads. Read `half` of
         // key group g, head-dim block b: this lane supplies row 16 g + 8 half +
@@ -149,7 +129,7 @@ struct FwdWave {
                 for (int b = 0; b < C::DB; ++b) {
                     const int r = 16 * g + 8 * hf + src_r;
                     const int d = 32 * b + src_d;
-                    voff[g][hf][b] = r * C::ROWB + 16 * ((d / 8) ^ vswz<D>(r)) + 2 * (d % 8);
+                    voff[g][hf][b] = tile_off<D>(r, d);
                 }
         m_run = -INFINITY;
         l_run = 0.f;
@@ -163,8 +143,8 @@ struct FwdWave {
             const size_t row = (size_t)min(kbase + ld_row[i], N - 1) * D;
             char* kdst = sKd + i * (C::NT * 16) + wave * 1024;
             char* vdst = sVd + i * (C::NT * 16) + wave * 1024;
-            __builtin_amdgcn_global_load_lds(Kh + row + ld_kcol[i], kdst, 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(Vh + row + ld_vcol[i], vdst, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(Kh + row + ld_col[i], kdst, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(Vh + row + ld_col[i], vdst, 16, 0, 0);
         }
     }
 

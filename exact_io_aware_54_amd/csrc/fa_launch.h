@@ -17,7 +17,7 @@ hipError_t launch_fwd_fp8(int d, bool causal, const void* q8, const void* k8, co
                           hipStream_t stream);
 hipError_t launch_bwd(int dtype, int d, bool causal, const void* q, const void* k, const void* v,
                       const void* o, const float* lse, const void* dO, void* dq, void* dk,
-                      void* dv, float* dq_acc, float* delta, int BH, int N, float scale,
-                      int stages, hipStream_t stream);  // stages: bit 0 pre, 1 main, 2 dQ convert
+                      void* dv, float* delta, float* lse2, int BH, int N, float scale,
+                      int stages, hipStream_t stream);  // stages: bit 0 pre, 1 dK/dV, 2 dQ
 
 }  // namespace fa

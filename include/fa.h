@@ -93,9 +93,9 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v8,
                int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
 
 /*
- * Size in bytes of the scratch buffer fa_bwd needs: a float32 dQ accumulator
- * [B,H,N,d] plus the float32 row terms D_i = sum_k dO_ik O_ik [B,H,N]. Returns
- * 0 for invalid shapes.
+ * Size in bytes of the scratch buffer fa_bwd needs: two float32 vectors of
+ * B*H*N entries, the row terms D_i = sum_k dO_ik O_ik and LSE_i * log2(e)
+ * (each padded to 256 bytes). Returns 0 for invalid shapes.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
 
@@ -111,8 +111,8 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
  *   dq, dk, dv [B,H,N,d] of `dtype`, written.
  *   workspace  device scratch of at least fa_bwd_workspace_bytes(B,H,N,d)
  *              bytes, 256-byte aligned; overwritten (no initial value needed).
- * The dQ accumulation uses float32 atomics, so dQ may differ in the last bits
- * from run to run; dK and dV are deterministic.
+ * dK/dV and dQ are produced by two separate passes over the score tiles (no
+ * atomics), so all three outputs are bitwise deterministic.
  */
 int fa_bwd(int dtype, const void* q, const void* k, const void* v, const void* o,
            const float* lse, const void* dO, void* dq, void* dk, void* dv,
@@ -122,14 +122,14 @@ int fa_bwd(int dtype, const void* q, const void* k, const void* v, const void* o
 /*
  * One of the three launches that make up fa_bwd, for callers that time or
  * schedule them separately. Same arguments and validation as fa_bwd, plus
- *   stage 1: D_i = sum_k dO_ik O_ik into the workspace, and the workspace's
- *            float32 dQ accumulator set to zero;
- *   stage 2: the main kernel -- recompute P and dS tile by tile, write dK and
- *            dV, add scale * dS K into the dQ accumulator (float32 atomics);
- *   stage 3: convert the dQ accumulator to `dtype` into dq.
- * Calling stages 1, 2, 3 in order on one stream is exactly fa_bwd. Stage 2
- * needs stage 1's workspace contents; stage 3 needs stage 2's. Any other
- * stage value returns FA_ERR_ARG.
+ *   stage 1: D_i = sum_k dO_ik O_ik and LSE_i * log2(e) into the workspace;
+ *   stage 2: per block of keys, recompute P and dS tile by tile and write
+ *            dK and dV;
+ *   stage 3: per block of queries, recompute P and dS tile by tile and
+ *            write dQ.
+ * Calling stages 1, 2, 3 in order on one stream is exactly fa_bwd. Stages 2
+ * and 3 need stage 1's workspace contents and are independent of each
+ * other. Any other stage value returns FA_ERR_ARG.
  */
 int fa_bwd_stage(int stage, int dtype, const void* q, const void* k, const void* v,
                  const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv,
