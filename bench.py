@@ -64,7 +64,7 @@ def traffic_for(kernel):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(q, k, v, do, scale, causal, budget_s, max_heads=16):
+def cpu_baseline(q, k, v, do, scale, causal, budget_s, max_heads=96):
     """Time the float64 oracle on whole heads of the workload until budget_s is spent."""
     import numpy as np
     import oracle
