@@ -11,14 +11,15 @@
 //
 // Three launches on the caller's stream:
 //  1. bwd_pre: per row, D_i (fp32) and LSE_i * log2(e) into the workspace.
-//  2. bwd_dkdv: one workgroup per (batch*head, block of 128 keys). Each of
-//     its four wavefronts keeps its 32 keys' K and V rows in registers (B
-//     operands) and their dK^T, dV^T in MFMA accumulators for the whole
-//     kernel, and walks the query blocks of 64 rows (causal: from the
-//     diagonal on). Per block: S = Q K^T and dP = dO V^T with the key index
+//  2. bwd_dkdv: one workgroup of eight wavefronts per (batch*head, block of
+//     128 keys), walking the query blocks of 64 rows (causal: from the
+//     diagonal on). K and V of the block stay in LDS; each wave owns 32 keys x
+//     32 queries of every block and keeps partial dK^T, dV^T in MFMA
+//     accumulators. Per block: S = Q K^T and dP = dO V^T with the key index
 //     across lanes and the query index in registers, P and dS in registers,
 //     then dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read straight
-//     out of the row-major Q / dO tiles by transposing LDS reads.
+//     out of the row-major Q / dO tiles by transposing LDS reads. The two
+//     waves sharing a key group sum their partials through LDS at the end.
 //  3. bwd_dq: one workgroup per (batch*head, block of 128 queries), shaped
 //     like the forward: Q and dO rows of the wave's 32 queries stay in
 //     registers, K/V tiles stream through LDS; per tile S^T = K Q^T,
@@ -75,16 +76,25 @@ bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO, const float* _
 }
 
 // ---------------------------------------------------------------- 2. dK, dV
+// Eight wavefronts per workgroup, two per SIMD: wave w owns key group
+// kg = w % 4 (32 keys) and query subtile qs = w / 4 (32 of the block's 64
+// queries). K and V of the block's 128 keys sit in LDS for the whole kernel
+// and are read as MFMA B operands; each wave keeps partial dK^T, dV^T for its
+// keys over its half of the queries, and the two halves are summed through
+// LDS at the end.
 template <int D>
 struct DkdvTile {
-    static constexpr int BN = 128;               // keys per workgroup (4 waves x 32)
-    static constexpr int BM = 64;                // queries per step
-    static constexpr int NT = 256;
+    static constexpr int BN = 128;               // keys per workgroup (4 key groups x 32)
+    static constexpr int BM = 64;                // queries per step (2 subtiles x 32)
+    static constexpr int NT = 512;               // 8 waves
     static constexpr int ROWB = 2 * D;
-    static constexpr int TILEB = BM * ROWB;      // bytes of one Q (or dO) tile
-    static constexpr int NLOAD = TILEB / (NT * 16);
+    static constexpr int QTILEB = BM * ROWB;     // bytes of one Q (or dO) tile
+    static constexpr int KTILEB = BN * ROWB;     // bytes of the K (or V) block
+    static constexpr int NLOADQ = QTILEB / (NT * 16);
+    static constexpr int NLOADK = KTILEB / (NT * 16);
     static constexpr int KS = D / 16;
     static constexpr int DB = D / 32;
+    static constexpr int PARTB = 32 * D * 4;     // bytes of one key group's fp32 partial
 };
 
 template <typename T, int D, bool CAUSAL>
@@ -97,17 +107,16 @@ struct DkdvWave {
     const T* dOh;
     const float* lse2h;
     const float* delh;
-    int N, tid, lane, wave, l32, h, key0, key;
+    int N, tid, lane, wave, l32, h, kg, qs, key0, key;
     float c;
-    V8 kf[C::KS], vf[C::KS];         // B operands: K and V rows of this lane's key
-    int ld_row[C::NLOAD], ld_col[C::NLOAD];
-    int roff[2][C::KS];              // 16-byte row reads of Q / dO (query 32 qs + l32)
-    int toff[2][2][2][C::DB];        // transposing reads [qs][g2][half][b]
-    f32x16 dkacc[C::DB], dvacc[C::DB];  // dK^T, dV^T: head dim in registers, key = lane
+    int ldq_row[C::NLOADQ], ldq_col[C::NLOADQ];
+    int roff[C::KS];                 // 16-byte row reads of Q / dO rows 32 qs + l32
+    int koff[C::KS];                 // 16-byte row reads of K / V rows 32 kg + l32 (B operands)
+    int toff[2][C::DB];              // transposing reads [half][b] (query group 0; +16 rows for g2 = 1)
+    f32x16 dkacc[C::DB], dvacc[C::DB];  // partial dK^T, dV^T: head dim in registers, key = lane
 
-    __device__ __forceinline__ void init(const T* Qh_, const T* Kh, const T* Vh, const T* dOh_,
-                                         const float* lse2h_, const float* delh_, int N_, int kb,
-                                         float c_) {
+    __device__ __forceinline__ void init(const T* Qh_, const T* dOh_, const float* lse2h_,
+                                         const float* delh_, int N_, int kb, float c_) {
         Qh = Qh_;
         dOh = dOh_;
         lse2h = lse2h_;
@@ -119,44 +128,34 @@ struct DkdvWave {
         wave = tid >> 6;
         l32 = lane & 31;
         h = lane >> 5;
-        key0 = kb * C::BN + 32 * wave;
+        kg = wave & 3;
+        qs = wave >> 2;
+        key0 = kb * C::BN + 32 * kg;
         key = key0 + l32;
-        const int kr = min(key, N - 1);
-        const V8* ks = reinterpret_cast<const V8*>(Kh + (size_t)kr * D + 8 * h);
-        const V8* vs = reinterpret_cast<const V8*>(Vh + (size_t)kr * D + 8 * h);
 #pragma unroll
-        for (int s = 0; s < C::KS; ++s) {
-            kf[s] = ks[2 * s];
-            vf[s] = vs[2 * s];
-        }
-#pragma unroll
-        for (int i = 0; i < C::NLOAD; ++i) {
+        for (int i = 0; i < C::NLOADQ; ++i) {
             const int byte = i * (C::NT * 16) + tid * 16;
             const int r = byte / C::ROWB, p = (byte % C::ROWB) / 16;
-            ld_row[i] = r;
-            ld_col[i] = (p ^ tile_swz<D>(r)) * 8;
+            ldq_row[i] = r;
+            ldq_col[i] = (p ^ tile_swz<D>(r)) * 8;
         }
 #pragma unroll
-        for (int qs = 0; qs < 2; ++qs)
-#pragma unroll
-            for (int s = 0; s < C::KS; ++s) roff[qs][s] = tile_off<D>(32 * qs + l32, 16 * s + 8 * h);
+        for (int s = 0; s < C::KS; ++s) {
+            roff[s] = tile_off<D>(32 * qs + l32, 16 * s + 8 * h);
+            koff[s] = tile_off<D>(32 * kg + l32, 16 * s + 8 * h);
+        }
         // transposing reads: this lane supplies row 32 qs + 16 g2 + 8 half + 4 h +
         // (lane % 16) / 4 and head dims 32 b + 16 ((lane / 16) % 2) + 4 (lane % 4);
         // it receives head dim 32 b + lane % 32 at queries 32 qs + 16 g2 + 8 half
         // + 4 h + 0..3, the order of registers 8 g2 + 4 half + 0..3 of the
-        // score accumulator of query subtile qs.
+        // score accumulator.
         const int src_r = 4 * h + (lane & 15) / 4;
         const int src_d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
-        for (int qs = 0; qs < 2; ++qs)
+        for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-            for (int g2 = 0; g2 < 2; ++g2)
-#pragma unroll
-                for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-                    for (int b = 0; b < C::DB; ++b)
-                        toff[qs][g2][hf][b] =
-                            tile_off<D>(32 * qs + 16 * g2 + 8 * hf + src_r, 32 * b + src_d);
+            for (int b = 0; b < C::DB; ++b)
+                toff[hf][b] = tile_off<D>(32 * qs + 8 * hf + src_r, 32 * b + src_d);
 #pragma unroll
         for (int b = 0; b < C::DB; ++b) {
             dkacc[b] = f32x16{};
@@ -164,87 +163,126 @@ struct DkdvWave {
         }
     }
 
+    // All rows of the key block into the K / V tiles (rows past N re-read N-1).
+    __device__ __forceinline__ void issue_kv(const T* Kh, const T* Vh, int kbase, char* sK,
+                                             char* sV) const {
+#pragma unroll
+        for (int i = 0; i < C::NLOADK; ++i) {
+            const int byte = i * (C::NT * 16) + tid * 16;
+            const int r = byte / C::ROWB, p = (byte % C::ROWB) / 16;
+            const size_t row = (size_t)min(kbase + r, N - 1) * D + (p ^ tile_swz<D>(r)) * 8;
+            const int o = i * (C::NT * 16) + wave * 1024;
+            __builtin_amdgcn_global_load_lds(Kh + row, sK + o, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(Vh + row, sV + o, 16, 0, 0);
+        }
+    }
+
     // Q and dO rows [qbase, qbase + BM) and their LSE2 / D into one buffer set.
     __device__ __forceinline__ void issue(int qbase, char* sQd, char* sGd, float* sLd,
                                           float* sDd) const {
 #pragma unroll
-        for (int i = 0; i < C::NLOAD; ++i) {
-            const size_t row = (size_t)min(qbase + ld_row[i], N - 1) * D;
+        for (int i = 0; i < C::NLOADQ; ++i) {
+            const size_t row = (size_t)min(qbase + ldq_row[i], N - 1) * D;
             const int o = i * (C::NT * 16) + wave * 1024;
-            __builtin_amdgcn_global_load_lds(Qh + row + ld_col[i], sQd + o, 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(dOh + row + ld_col[i], sGd + o, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(Qh + row + ldq_col[i], sQd + o, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(dOh + row + ldq_col[i], sGd + o, 16, 0, 0);
         }
         const int r = min(qbase + lane, N - 1);
         if (wave == 0) __builtin_amdgcn_global_load_lds(lse2h + r, sLd, 4, 0, 0);
         if (wave == 1) __builtin_amdgcn_global_load_lds(delh + r, sDd, 4, 0, 0);
     }
 
-    __device__ __forceinline__ void step(int ib, int nqb, const char* sQ, const char* sG,
-                                         const float* sL, const float* sD, char* nQ, char* nG,
-                                         float* nL, float* nD) {
+    __device__ __forceinline__ void step(int ib, int nqb, const char* sK, const char* sV,
+                                         const char* sQ, const char* sG, const float* sL,
+                                         const float* sD, char* nQ, char* nG, float* nL,
+                                         float* nD) {
         const int qbase = ib * C::BM;
         __builtin_amdgcn_s_waitcnt(kVmcntZero);
         __syncthreads();
         if (ib + 1 < nqb) issue(qbase + C::BM, nQ, nG, nL, nD);
-        if (CAUSAL && key0 > qbase + C::BM - 1) return;  // every query of the block precedes every key
+        const int qb0 = qbase + 32 * qs;  // first query of this wave's subtile
+        if (CAUSAL && key0 > qb0 + 31) return;  // every query of the subtile precedes every key
 
+        // S = Q K^T and dP = dO V^T (lane = key, register r = query qb0 + acc_row(r, h))
+        f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
-        for (int qs = 0; qs < 2; ++qs) {
-            f32x16 sacc = f32x16{}, pacc = f32x16{};
+        for (int s = 0; s < C::KS; ++s) {
+            const V8 aq = *reinterpret_cast<const V8*>(sQ + roff[s]);
+            const V8 bk = *reinterpret_cast<const V8*>(sK + koff[s]);
+            const V8 ag = *reinterpret_cast<const V8*>(sG + roff[s]);
+            const V8 bv = *reinterpret_cast<const V8*>(sV + koff[s]);
+            sacc = mfma32(aq, bk, sacc);
+            pacc = mfma32(ag, bv, pacc);
+        }
+        const bool need_mask = key0 + 31 >= N || qb0 + 31 >= N || (CAUSAL && key0 + 31 > qb0);
+        const int lo = key - qb0 - 4 * h;   // causal-visible iff const(r) >= lo
+        const int hi = N - qb0 - 4 * h;     // query < N iff const(r) < hi
+        const bool kvalid = key < N;
+        // P = 2^(s c - LSE2), dS = P (dP - D); masked entries get P = 0
 #pragma unroll
-            for (int s = 0; s < C::KS; ++s) {
-                const V8 aq = *reinterpret_cast<const V8*>(sQ + roff[qs][s]);
-                const V8 ag = *reinterpret_cast<const V8*>(sG + roff[qs][s]);
-                sacc = mfma32(aq, kf[s], sacc);
-                pacc = mfma32(ag, vf[s], pacc);
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 lq = *reinterpret_cast<const f32x4*>(sL + 32 * qs + 8 * r4 + 4 * h);
+            const f32x4 dq = *reinterpret_cast<const f32x4*>(sD + 32 * qs + 8 * r4 + 4 * h);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * r4 + i;
+                float l2 = lq[i];
+                if (need_mask) {
+                    const int cr = 8 * r4 + i;
+                    const bool vis = kvalid && cr < hi && (!CAUSAL || cr >= lo);
+                    if (!vis) l2 = INFINITY;
+                }
+                const float p = fast_exp2(fmaf(sacc[r], c, -l2));
+                sacc[r] = p;
+                pacc[r] = p * (pacc[r] - dq[i]);
             }
-            // lane = key, register r = query 32 qs + acc_row(r, h) of the block
-            float lq[16], dq[16];
+        }
+        V8 pf[2], sf[2];
+        pf[0] = pack8<T>(sacc, 0);
+        pf[1] = pack8<T>(sacc, 8);
+        sf[0] = pack8<T>(pacc, 0);
+        sf[1] = pack8<T>(pacc, 8);
+        // dV^T += dO^T P and dK^T += Q^T dS
+#pragma unroll
+        for (int g2 = 0; g2 < 2; ++g2)
+#pragma unroll
+            for (int b = 0; b < C::DB; ++b) {
+                const int o0 = toff[0][b] + g2 * 16 * C::ROWB, o1 = toff[1][b] + g2 * 16 * C::ROWB;
+                const V8 at = tr_read8<V8>(sG, o0, o1);
+                dvacc[b] = mfma32(at, pf[g2], dvacc[b]);
+                const V8 aq = tr_read8<V8>(sQ, o0, o1);
+                dkacc[b] = mfma32(aq, sf[g2], dkacc[b]);
+            }
+    }
+
+    // Partials of query subtile 1 -> LDS (dK into pk, dV into pv, one region per key group).
+    __device__ __forceinline__ void put_partials(char* pk, char* pv) const {
+#pragma unroll
+        for (int b = 0; b < C::DB; ++b)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
-                const f32x4 a = *reinterpret_cast<const f32x4*>(sL + 32 * qs + 8 * r4 + 4 * h);
-                const f32x4 b = *reinterpret_cast<const f32x4*>(sD + 32 * qs + 8 * r4 + 4 * h);
+                const int o = ((b * 4 + r4) * 64 + lane) * 16;
+                *reinterpret_cast<f32x4*>(pk + o) =
+                    f32x4{dkacc[b][4 * r4], dkacc[b][4 * r4 + 1], dkacc[b][4 * r4 + 2], dkacc[b][4 * r4 + 3]};
+                *reinterpret_cast<f32x4*>(pv + o) =
+                    f32x4{dvacc[b][4 * r4], dvacc[b][4 * r4 + 1], dvacc[b][4 * r4 + 2], dvacc[b][4 * r4 + 3]};
+            }
+    }
+
+    __device__ __forceinline__ void add_partials(const char* pk, const char* pv) {
+#pragma unroll
+        for (int b = 0; b < C::DB; ++b)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int o = ((b * 4 + r4) * 64 + lane) * 16;
+                const f32x4 a = *reinterpret_cast<const f32x4*>(pk + o);
+                const f32x4 v = *reinterpret_cast<const f32x4*>(pv + o);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    lq[4 * r4 + i] = a[i];
-                    dq[4 * r4 + i] = b[i];
+                    dkacc[b][4 * r4 + i] += a[i];
+                    dvacc[b][4 * r4 + i] += v[i];
                 }
             }
-            const int qb0 = qbase + 32 * qs;
-            const bool need_mask = key0 + 31 >= N || qb0 + 31 >= N || (CAUSAL && key0 + 31 > qb0);
-            if (need_mask) {
-                // query qb0 + 8 (r / 4) + (r % 4) + 4 h is valid iff < N and (causal) >= key
-                const int lo = key - qb0 - 4 * h;   // const(r) >= lo when causal-visible
-                const int hi = N - qb0 - 4 * h;     // const(r) < hi when query < N
-                const bool kvalid = key < N;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int cr = 8 * (r >> 2) + (r & 3);
-                    const bool vis = kvalid && cr < hi && (!CAUSAL || cr >= lo);
-                    if (!vis) lq[r] = INFINITY;  // P = 2^(s c - inf) = 0
-                }
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = fast_exp2(fmaf(sacc[r], c, -lq[r]));
-                sacc[r] = p;
-                pacc[r] = p * (pacc[r] - dq[r]);
-            }
-            V8 pf[2], sf[2];
-            pf[0] = pack8<T>(sacc, 0);
-            pf[1] = pack8<T>(sacc, 8);
-            sf[0] = pack8<T>(pacc, 0);
-            sf[1] = pack8<T>(pacc, 8);
-#pragma unroll
-            for (int g2 = 0; g2 < 2; ++g2)
-#pragma unroll
-                for (int b = 0; b < C::DB; ++b) {
-                    const V8 at = tr_read8<V8>(sG, toff[qs][g2][0][b], toff[qs][g2][1][b]);
-                    dvacc[b] = mfma32(at, pf[g2], dvacc[b]);
-                    const V8 aq = tr_read8<V8>(sQ, toff[qs][g2][0][b], toff[qs][g2][1][b]);
-                    dkacc[b] = mfma32(aq, sf[g2], dkacc[b]);
-                }
-        }
     }
 
     __device__ __forceinline__ void finish(T* dKh, T* dVh, float scale) {
@@ -268,20 +306,24 @@ struct DkdvWave {
 };
 
 template <typename T, int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(512, 1)
 bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                 const T* __restrict__ dO, const float* __restrict__ lse2,
                 const float* __restrict__ delta, T* __restrict__ dK, T* __restrict__ dV, int BH,
                 int N, int nkb, float scale, float c) {
     using C = DkdvTile<D>;
-    __shared__ __attribute__((aligned(1024))) char sQ0[C::TILEB];
-    __shared__ __attribute__((aligned(1024))) char sQ1[C::TILEB];
-    __shared__ __attribute__((aligned(1024))) char sG0[C::TILEB];
-    __shared__ __attribute__((aligned(1024))) char sG1[C::TILEB];
+    __shared__ __attribute__((aligned(1024))) char sK[C::KTILEB];
+    __shared__ __attribute__((aligned(1024))) char sV[C::KTILEB];
+    __shared__ __attribute__((aligned(1024))) char sQ0[C::QTILEB];
+    __shared__ __attribute__((aligned(1024))) char sQ1[C::QTILEB];
+    __shared__ __attribute__((aligned(1024))) char sG0[C::QTILEB];
+    __shared__ __attribute__((aligned(1024))) char sG1[C::QTILEB];
     __shared__ __attribute__((aligned(256))) float sL0[C::BM];
     __shared__ __attribute__((aligned(256))) float sL1[C::BM];
     __shared__ __attribute__((aligned(256))) float sD0[C::BM];
     __shared__ __attribute__((aligned(256))) float sD1[C::BM];
+    static_assert(2 * C::PARTB <= C::KTILEB && C::PARTB <= C::QTILEB,
+                  "partial sums must fit the K/V and Q/dO tiles");
 
     const int L = xcd_remap(blockIdx.x, BH * nkb);
     const int bh = L / nkb;
@@ -290,15 +332,25 @@ bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     const size_t rowbase = (size_t)bh * N;
 
     DkdvWave<T, D, CAUSAL> w;
-    w.init(Q + head, K + head, V + head, dO + head, lse2 + rowbase, delta + rowbase, N, kb, c);
+    w.init(Q + head, dO + head, lse2 + rowbase, delta + rowbase, N, kb, c);
     const int nqb = (N + C::BM - 1) / C::BM;
     const int i0 = CAUSAL ? (kb * C::BN) / C::BM : 0;
+    w.issue_kv(K + head, V + head, kb * C::BN, sK, sV);
     w.issue(i0 * C::BM, sQ0, sG0, sL0, sD0);
     for (int ib = i0; ib < nqb; ib += 2) {
-        w.step(ib, nqb, sQ0, sG0, sL0, sD0, sQ1, sG1, sL1, sD1);
-        if (ib + 1 < nqb) w.step(ib + 1, nqb, sQ1, sG1, sL1, sD1, sQ0, sG0, sL0, sD0);
+        w.step(ib, nqb, sK, sV, sQ0, sG0, sL0, sD0, sQ1, sG1, sL1, sD1);
+        if (ib + 1 < nqb) w.step(ib + 1, nqb, sK, sV, sQ1, sG1, sL1, sD1, sQ0, sG0, sL0, sD0);
     }
-    w.finish(dK + head, dV + head, scale);
+    // sum the two query halves: subtile-1 waves park their partials in LDS
+    __syncthreads();
+    char* pk = (w.kg < 2 ? sK : sV) + (w.kg & 1) * C::PARTB;
+    char* pv = w.kg == 0 ? sQ0 : w.kg == 1 ? sQ1 : w.kg == 2 ? sG0 : sG1;
+    if (w.qs == 1) w.put_partials(pk, pv);
+    __syncthreads();
+    if (w.qs == 0) {
+        w.add_partials(pk, pv);
+        w.finish(dK + head, dV + head, scale);
+    }
 }
 
 // ---------------------------------------------------------------- 3. dQ
@@ -510,7 +562,7 @@ hipError_t launch_typed(const void* q, const void* k, const void* v, const void*
     }
     if (stages & 2) {
         const int nkb = (N + DkdvTile<D>::BN - 1) / DkdvTile<D>::BN;
-        hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3(BH * nkb), dim3(256), 0, stream,
+        hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3(BH * nkb), dim3(DkdvTile<D>::NT), 0, stream,
                            tq, tk, tv, tdo, lse2, delta, static_cast<T*>(dk), static_cast<T*>(dv),
                            BH, N, nkb, scale, c);
         if ((e = hipGetLastError()) != hipSuccess) return e;
