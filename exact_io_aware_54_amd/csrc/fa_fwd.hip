@@ -4,8 +4,8 @@
 // BM query rows and K/V into blocks of BN keys; one workgroup owns one query
 // block of one (batch, head) and walks the K/V blocks in order (section
 // "Flash Attention 2": Q-block outer loop, parallel over batch x heads x query
-// blocks). Each K/V tile is staged once in LDS and shared by the four
-// wavefronts. Per tile: scores, running row max, exponentials against the
+// blocks). Each K/V tile is staged once in LDS and shared by the workgroup's
+// four or eight wavefronts. Per tile: scores, running row max, exponentials against the
 // max, rescaled running sum and rescaled output (sections "Flash Attention:
 // The Key Insight" and "The Tiling Algorithm"). The output stays unnormalised
 // and is divided by the row sum once at the end (the reduced non-matmul work
@@ -45,24 +45,29 @@ namespace {
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-template <int D>
+// NW wavefronts of 32 queries per workgroup share each K/V tile of BN keys.
+template <int D, int NW_>
 struct FwdTile {
-    static constexpr int BM = 128;                 // queries per workgroup (4 waves x 32)
+    static constexpr int NW = NW_;
+    static constexpr int BM = 32 * NW;             // queries per workgroup
     static constexpr int BN = 64;                  // keys per K/V tile
-    static constexpr int NT = 256;                 // threads per workgroup
+    static constexpr int NT = 64 * NW;             // threads per workgroup
+    static constexpr int NSUB = BN / 32;           // 32-key score subtiles per tile
+    static constexpr int NG = BN / 16;             // 16-key groups (P V MFMAs per head-dim block)
     static constexpr int ROWB = D * 2;             // bytes per K/V row
     static constexpr int TILEB = BN * ROWB;        // bytes per K (or V) tile
     static constexpr int NLOAD = TILEB / (NT * 16);  // direct loads per thread per tile
     static constexpr int KS = D / 16;              // MFMA k-steps over the head dim
     static constexpr int DB = D / 32;              // 32-row blocks of O^T
+    static_assert(NLOAD >= 1 && TILEB % (NT * 16) == 0, "tile must split into whole direct loads");
 };
 
 constexpr float kRescaleThreshold = 8.f;  // log2 units: refresh m when it grows by > 2^8
 
 // Per-wavefront state of the forward kernel and its steps.
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, int NW>
 struct FwdWave {
-    using C = FwdTile<D>;
+    using C = FwdTile<D, NW>;
     using V8 = typename Vec<T>::x8;
     using V4 = typename Vec<T>::x4;
 
@@ -72,8 +77,8 @@ struct FwdWave {
     float c;
     V8 qf[C::KS];               // B operand of S^T = K Q^T (d = 16 s + 8 h + j)
     int ld_row[C::NLOAD], ld_col[C::NLOAD];
-    int koff[2][C::KS];         // LDS byte offsets of the K operand reads
-    int voff[4][2][C::DB];      // LDS byte offsets of the V^T transposing reads
+    int koff[C::KS];            // LDS byte offsets of the K operand reads (rows l32; +32 rows per subtile)
+    int voff[2][C::DB];         // LDS byte offsets of the V^T transposing reads (key group 0; +16 rows per group)
     float m_run, l_run;         // running (reference) max of s * c and this lane's sum
     f32x16 oacc[C::DB];         // O^T accumulators (head dim 32 b + row, query = lane)
 
@@ -107,13 +112,10 @@ struct FwdWave {
             ld_row[i] = r;
             ld_col[i] = (p ^ tile_swz<D>(r)) * 8;
         }
-        // K (A side of S^T): key 32 c2 + l32, chunk 2 s + h.
+        // K (A side of S^T): key 32 c2 + l32, chunk 2 s + h. The swizzle repeats
+        // every 16 rows, so subtile c2 is koff + 32 c2 rows.
 #pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-            for (int s = 0; s < C::KS; ++s) {
-                koff[c2][s] = tile_off<D>(32 * c2 + l32, 16 * s + 8 * h);
-            }
+        for (int s = 0; s < C::KS; ++s) koff[s] = tile_off<D>(l32, 16 * s + 8 * h);
         // V^T (A side of O^T = V^T P^T) via transposing reads. Read `half` of
         // key group g, head-dim block b: this lane supplies row 16 g + 8 half +
         // 4 h + (lane % 16) / 4, columns 32 b + 16 ((lane / 16) % 2) + 4 (lane %
@@ -122,15 +124,9 @@ struct FwdWave {
         const int src_r = 4 * h + (lane & 15) / 4;
         const int src_d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
+        for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-                for (int b = 0; b < C::DB; ++b) {
-                    const int r = 16 * g + 8 * hf + src_r;
-                    const int d = 32 * b + src_d;
-                    voff[g][hf][b] = tile_off<D>(r, d);
-                }
+            for (int b = 0; b < C::DB; ++b) voff[hf][b] = tile_off<D>(8 * hf + src_r, 32 * b + src_d);
         m_run = -INFINITY;
         l_run = 0.f;
 #pragma unroll
@@ -142,7 +138,7 @@ struct FwdWave {
         for (int i = 0; i < C::NLOAD; ++i) {
             const size_t row = (size_t)min(kbase + ld_row[i], N - 1) * D;
             char* kdst = sKd + i * (C::NT * 16) + wave * 1024;
-            char* vdst = sVd + i * (C::NT * 16) + wave * 1024;
+            char* vdst = sVd + i * (C::NT * 16) + wave * 1024;  // this wave's 1 KiB of load i
             __builtin_amdgcn_global_load_lds(Kh + row + ld_col[i], kdst, 16, 0, 0);
             __builtin_amdgcn_global_load_lds(Vh + row + ld_col[i], vdst, 16, 0, 0);
         }
@@ -161,14 +157,14 @@ struct FwdWave {
 
         const bool active = !CAUSAL || kbase <= q0 + 31;
         if (!active) return;
-        f32x16 s[2];
-        s[0] = f32x16{};
-        s[1] = f32x16{};
+        f32x16 s[C::NSUB];
+#pragma unroll
+        for (int c2 = 0; c2 < C::NSUB; ++c2) s[c2] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2) {
-                const V8 a = *reinterpret_cast<const V8*>(kb + koff[c2][ks]);
+            for (int c2 = 0; c2 < C::NSUB; ++c2) {
+                const V8 a = *reinterpret_cast<const V8*>(kb + koff[ks] + c2 * 32 * C::ROWB);
                 s[c2] = mfma32(a, qf[ks], s[c2]);
             }
         // mask: key kbase + 32 c2 + acc_row(r, h) is visible iff it is <= lim + 4 h + kbase
@@ -176,7 +172,7 @@ struct FwdWave {
         if (need_mask) {
             const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - kbase - 4 * h;
 #pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2)
+            for (int c2 = 0; c2 < C::NSUB; ++c2)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     if (32 * c2 + 8 * (r >> 2) + (r & 3) > lim) s[c2][r] = -INFINITY;
@@ -185,7 +181,9 @@ struct FwdWave {
 #pragma unroll
         for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+        for (int c2 = 1; c2 < C::NSUB; ++c2)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[c2][r]);
         mx = wave_half_max(mx) * c;
         if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleThreshold) != 0) {
             const float m_new = fmaxf(m_run, mx);
@@ -199,7 +197,7 @@ struct FwdWave {
         }
         float rs = 0.f;
 #pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2)
+        for (int c2 = 0; c2 < C::NSUB; ++c2)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const float p = fast_exp2(fmaf(s[c2][r], c, -m_run));
@@ -208,17 +206,16 @@ struct FwdWave {
             }
         l_run += rs;
 
-        V8 pf[4];
-        pf[0] = pack8<T>(s[0], 0);
-        pf[1] = pack8<T>(s[0], 8);
-        pf[2] = pack8<T>(s[1], 0);
-        pf[3] = pack8<T>(s[1], 8);
+        V8 pf[C::NG];
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
+        for (int g = 0; g < C::NG; ++g) pf[g] = pack8<T>(s[g / 2], 8 * (g % 2));
+#pragma unroll
+        for (int g = 0; g < C::NG; ++g)
 #pragma unroll
             for (int b = 0; b < C::DB; ++b) {
-                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + voff[g][0][b]));
-                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + voff[g][1][b]));
+                const char* vg = vb + g * 16 * C::ROWB;
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vg + voff[0][b]));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vg + voff[1][b]));
                 const s16x4 w[2] = {lo, hi};
                 V8 a;
                 __builtin_memcpy(&a, w, sizeof(a));
@@ -245,11 +242,11 @@ struct FwdWave {
     }
 };
 
-template <typename T, int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, 2)
+template <typename T, int D, bool CAUSAL, int NW>
+__global__ void __launch_bounds__(64 * NW, 2)
 fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                 T* __restrict__ O, float* __restrict__ LSE, int BH, int N, int nqb, float c) {
-    using C = FwdTile<D>;
+    using C = FwdTile<D, NW>;
     // Two buffers per tensor as four separate LDS objects: the compiler can
     // then tell that the loads in flight into one buffer never alias the
     // reads of the other, and does not wait for them before every read.
@@ -263,7 +260,7 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     const int qb = CAUSAL ? (nqb - 1 - L % nqb) : (L % nqb);
     const size_t head = (size_t)bh * N * D;
 
-    FwdWave<T, D, CAUSAL> w;
+    FwdWave<T, D, CAUSAL, NW> w;
     w.init(Q + head, K + head, V + head, N, qb, c);
     w.issue_tile(0, sK0, sV0);
     for (int kt = 0; kt < w.nkt; kt += 2) {
@@ -273,17 +270,29 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     w.finish(O + head, LSE == nullptr ? nullptr : LSE + (size_t)bh * N);
 }
 
-template <typename T, int D, bool CAUSAL>
-hipError_t launch_typed(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
-                        int N, float scale, hipStream_t stream) {
-    using C = FwdTile<D>;
+template <typename T, int D, bool CAUSAL, int NW>
+hipError_t launch_nw(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
+                     int N, float scale, hipStream_t stream) {
+    using C = FwdTile<D, NW>;
     const int nqb = (N + C::BM - 1) / C::BM;
     const dim3 grid(BH * nqb), block(C::NT);
-    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, CAUSAL>), grid, block, 0, stream,
+    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, CAUSAL, NW>), grid, block, 0, stream,
                        static_cast<const T*>(q), static_cast<const T*>(k),
                        static_cast<const T*>(v), static_cast<T*>(o), lse, BH, N, nqb,
                        scale * kLog2e);
     return hipGetLastError();
+}
+
+// Workgroup shape: eight waves (256 queries, one workgroup per CU, K/V tiles
+// shared by all eight) measured 5-6 % faster on non-causal and on causal
+// N >= 8192; four waves (128 queries, two workgroups per CU) are better for
+// shorter causal sequences, where 256-query blocks make the per-block work
+// too uneven.
+template <typename T, int D, bool CAUSAL>
+hipError_t launch_typed(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
+                        int N, float scale, hipStream_t stream) {
+    if (CAUSAL && N < 8192) return launch_nw<T, D, CAUSAL, 4>(q, k, v, o, lse, BH, N, scale, stream);
+    return launch_nw<T, D, CAUSAL, 8>(q, k, v, o, lse, BH, N, scale, stream);
 }
 
 template <typename T>
