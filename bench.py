@@ -16,6 +16,11 @@ Prints ONE JSON line on stdout. Besides the contract fields it carries
   breakdown    -- per-launch times and TFLOPS.
 `--suite PATH` additionally times every workload of the parity suite and
 writes one JSON line per workload to PATH.
+`--compare-standard PATH` runs only the comparison of the IO-aware forward with
+the standard (materialising) forward that the pages' exercise describes
+(B=1, H=32, d=128, fp16 random normals, N = 2048, 8192, 32768; 3 warm-up and
+10 timed runs each; peak device memory from torch's allocator) and writes one
+JSON line per sequence length to PATH.
 """
 
 import argparse
@@ -263,6 +268,61 @@ def run_suite(path, torch, fa, inputs):
     out.close()
 
 
+def run_compare(path, torch, fa, inputs, lengths=(2048, 8192, 32768)):
+    """IO-aware forward vs standard forward: time and peak memory per length."""
+    B, H, d = 1, 32, 128
+    scale = d ** -0.5
+    out = open(path, "w")
+    for N in lengths:
+        seed = 1100 + N // 1024
+        print(f"[compare] N={N} seed={seed}", file=sys.stderr, flush=True)
+        q, k, v = (t.cuda() for t in inputs.draw_qkv(B, H, N, d, seed, torch.float16))
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        base = torch.cuda.memory_allocated()
+        rec = {"workload": f"fwd f16 B{B} H{H} N{N} d{d} non-causal", "seed": seed}
+        for name in ("flash", "standard"):
+            torch.cuda.empty_cache()
+            torch.cuda.reset_peak_memory_stats()
+            o = torch.empty_like(q)
+            if name == "flash":
+                lse = torch.empty((B, H, N), device="cuda", dtype=torch.float32)
+                fn = lambda: fa.fa_fwd(q, k, v, o, lse, scale, False)  # noqa: E731
+            else:
+                ws = torch.empty(fa.fa_std_workspace_bytes(B, H, N, d), device="cuda",
+                                 dtype=torch.uint8)
+                fn = lambda: fa.fa_std_fwd(q, k, v, o, ws, scale, False)  # noqa: E731
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(10):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 10
+            peak = torch.cuda.max_memory_allocated()
+            rec[name] = {"time_ms": round(ms, 3),
+                         "tflops": round(counted_flops(B, H, N, d, False) / (ms * 1e-3) / 1e12, 1),
+                         "peak_mib": round(peak / 2 ** 20, 1),
+                         "beyond_inputs_mib": round((peak - base) / 2 ** 20, 1)}
+            print(f"[compare]   {name}: {rec[name]}", file=sys.stderr, flush=True)
+            del fn, o
+            if name == "flash":
+                del lse
+            else:
+                del ws
+        rec["speedup"] = round(rec["standard"]["time_ms"] / rec["flash"]["time_ms"], 2)
+        rec["memory_ratio_beyond_inputs"] = round(
+            rec["standard"]["beyond_inputs_mib"] / rec["flash"]["beyond_inputs_mib"], 1)
+        print(json.dumps(rec), file=out, flush=True)
+        print(f"[compare] {json.dumps(rec)}", file=sys.stderr, flush=True)
+        del q, k, v
+        torch.cuda.empty_cache()
+    out.close()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -272,6 +332,10 @@ def main():
                     help="budget for the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--suite", metavar="PATH", help="also time every workload, JSON lines to PATH")
+    ap.add_argument("--compare-standard", metavar="PATH",
+                    help="only run the IO-aware vs standard forward comparison, JSON lines to PATH")
+    ap.add_argument("--compare-n", type=int, nargs="+", default=[2048, 8192, 32768],
+                    help="sequence lengths of --compare-standard")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device copy, the reference kernel for scaling "
                          "PMC byte counters")
@@ -282,6 +346,15 @@ def main():
               "communication, so the whole-job rate at N GPUs is N times the 1-GPU figure at "
               "the per-GPU head count; run with --gpus 1.", file=sys.stderr, flush=True)
         sys.exit(2)
+    if args.compare_standard:
+        import torch
+        import exact_io_aware_54_amd as fa
+        from exact_io_aware_54_amd import inputs
+        if not torch.cuda.is_available():
+            sys.exit("bench.py needs a GPU")
+        fa.load_library()
+        run_compare(args.compare_standard, torch, fa, inputs, args.compare_n)
+        return
     run_main(args)
 
 

@@ -9,9 +9,10 @@ in the library's kernels; there is no fallback path. If the library has not
 been built, calls raise ``RuntimeError``.
 
 Entry points: ``fa_fwd``, ``fa_fwd_fp8``, ``fa_bwd``, ``fa_bwd_stage``,
-``fa_bwd_workspace_bytes``,
+``fa_bwd_workspace_bytes``, ``fa_std_fwd``, ``fa_std_workspace_bytes``,
 ``fa_status_string``, ``fa_version``; ``forward`` / ``backward`` /
-``forward_fp8`` allocate outputs with torch and call them.
+``forward_fp8`` / ``forward_standard`` allocate outputs with torch and call
+them.
 """
 
 import ctypes
@@ -57,6 +58,10 @@ def load_library(path=None):
     lib.fa_bwd.restype = i
     lib.fa_bwd_stage.argtypes = [i] + lib.fa_bwd.argtypes
     lib.fa_bwd_stage.restype = i
+    lib.fa_std_workspace_bytes.argtypes = [i, i, i, i]
+    lib.fa_std_workspace_bytes.restype = sz
+    lib.fa_std_fwd.argtypes = [i, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, vp]
+    lib.fa_std_fwd.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -179,6 +184,25 @@ def fa_bwd_stage(stage, q, k, v, o, lse, do, dq, dk, dv, workspace, scale, causa
     _raise("fa_bwd_stage", st)
 
 
+def fa_std_workspace_bytes(B, H, N, d):
+    return int(load_library().fa_std_workspace_bytes(B, H, N, d))
+
+
+def fa_std_fwd(q, k, v, o, workspace, scale, causal, stream=None):
+    """Standard attention (S and P materialised in ``workspace``) into ``o``."""
+    import torch
+    lib = load_library()
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _check_bhnd(name, t, (B, H, N, d), q.dtype)
+    if workspace.dtype != torch.uint8 or not workspace.is_cuda:
+        raise TypeError("workspace must be a uint8 device tensor")
+    st = lib.fa_std_fwd(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(workspace),
+                        workspace.numel(), B, H, N, d, float(scale), int(bool(causal)),
+                        _stream(stream))
+    _raise("fa_std_fwd", st)
+
+
 # ------------------------------------------------- allocate-and-call conveniences
 
 def forward(q, k, v, scale=None, causal=False):
@@ -189,6 +213,17 @@ def forward(q, k, v, scale=None, causal=False):
     lse = torch.empty(q.shape[:-1], device=q.device, dtype=torch.float32)
     fa_fwd(q, k, v, o, lse, scale, causal)
     return o, lse
+
+
+def forward_standard(q, k, v, scale=None, causal=False):
+    """Allocate O and the N x N workspace with torch and run fa_std_fwd."""
+    import torch
+    B, H, N, d = q.shape
+    scale = d ** -0.5 if scale is None else scale
+    o = torch.empty_like(q)
+    ws = torch.empty(fa_std_workspace_bytes(B, H, N, d), device=q.device, dtype=torch.uint8)
+    fa_std_fwd(q, k, v, o, ws, scale, causal)
+    return o
 
 
 def forward_fp8(q8, k8, v8, descales, scale=None, causal=False):

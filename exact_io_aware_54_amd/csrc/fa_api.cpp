@@ -124,4 +124,24 @@ int fa_bwd_stage(int stage, int dtype, const void* q, const void* k, const void*
                       d, scale, causal, 1 << (stage - 1), stream);
 }
 
+size_t fa_std_workspace_bytes(int B, int H, int N, int d) {
+    if (check_shape(B, H, N, d) != FA_OK) return 0;
+    return (size_t)B * H * N * (size_t)N * 2;  // one 16-bit N x N matrix per head
+}
+
+int fa_std_fwd(int dtype, const void* q, const void* k, const void* v, void* o, void* workspace,
+               size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
+               hipStream_t stream) {
+    if (!q || !k || !v || !o || !workspace) return FA_ERR_NULL;
+    if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+    const int st = check_shape(B, H, N, d);
+    if (st != FA_OK) return st;
+    if ((int64_t)B * H > 65535) return FA_ERR_SHAPE;
+    if (!good_scale(scale)) return FA_ERR_ARG;
+    if (workspace_bytes < fa_std_workspace_bytes(B, H, N, d)) return FA_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255) != 0) return FA_ERR_WORKSPACE;
+    return status_of(
+        fa::launch_std(dtype, d, causal != 0, q, k, v, o, workspace, B * H, N, scale, stream));
+}
+
 }  // extern "C"

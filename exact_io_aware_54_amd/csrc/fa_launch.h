@@ -19,5 +19,7 @@ hipError_t launch_bwd(int dtype, int d, bool causal, const void* q, const void* 
                       const void* o, const float* lse, const void* dO, void* dq, void* dk,
                       void* dv, float* delta, float* lse2, int BH, int N, float scale,
                       int stages, hipStream_t stream);  // stages: bit 0 pre, 1 dK/dV, 2 dQ
+hipError_t launch_std(int dtype, int d, bool causal, const void* q, const void* k, const void* v,
+                      void* o, void* s, int BH, int N, float scale, hipStream_t stream);
 
 }  // namespace fa

@@ -56,7 +56,7 @@ typedef enum {
     FA_ERR_SHAPE = -2,      /* B, H or N < 1, or the tensor is too large         */
     FA_ERR_DTYPE = -3,      /* dtype not supported by this entry point           */
     FA_ERR_HEADDIM = -4,    /* d not in {64, 128}                                */
-    FA_ERR_WORKSPACE = -5,  /* workspace smaller than fa_bwd_workspace_bytes()   */
+    FA_ERR_WORKSPACE = -5,  /* workspace too small or not 256-byte aligned      */
     FA_ERR_HIP = -6,        /* the HIP runtime reported an error at launch       */
     FA_ERR_ARG = -7         /* a scalar argument is invalid (scale not finite or
                                not positive, descale not finite or <= 0)         */
@@ -135,6 +135,34 @@ int fa_bwd_stage(int stage, int dtype, const void* q, const void* k, const void*
                  const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv,
                  void* workspace, size_t workspace_bytes,
                  int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/*
+ * Size in bytes of the scratch buffer fa_std_fwd needs: the N x N score
+ * matrix of every (batch, head) in the 16-bit input type, B*H*N*N*2 bytes
+ * (S, then P written over it). Returns 0 for invalid shapes.
+ */
+size_t fa_std_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * Standard (materialising) attention forward, the baseline the IO-aware path
+ * is measured against ("11.11 Flash Attention", section "Standard Attention:
+ * Step by Step"): three passes through memory instead of one --
+ *   1. S = scale * Q K^T is written to `workspace` (16-bit, [B,H,N,N]);
+ *   2. each row is read back and overwritten with P = softmax(S_i) (causal:
+ *      P_ij = 0 for j > i);
+ *   3. O = P V reads P back.
+ * Same O as fa_fwd up to rounding (S and P are rounded to the input type);
+ * no LSE. Not the product path: it exists to reproduce the comparison of
+ * time and memory that the pages make.
+ *   dtype      FA_BF16 or FA_F16.
+ *   q, k, v, o [B,H,N,d] of `dtype` as in fa_fwd.
+ *   workspace  device scratch of at least fa_std_workspace_bytes(B,H,N,d)
+ *              bytes, 256-byte aligned; overwritten.
+ * Also FA_ERR_SHAPE if B*H > 65535 (grid limit of the score pass).
+ */
+int fa_std_fwd(int dtype, const void* q, const void* k, const void* v, void* o,
+               void* workspace, size_t workspace_bytes,
+               int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
 
 /* Human-readable text for a fa_status value (static storage, never NULL). */
 const char* fa_status_string(int status);

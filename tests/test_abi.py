@@ -117,3 +117,43 @@ def test_bwd_validation(lib):
     assert bwd(stage=0) == -7
     assert bwd(stage=4) == -7
     assert bwd(stage=2, wsb=0) == -5
+
+
+def test_std_workspace_bytes(lib):
+    # one 16-bit N x N score matrix per (batch, head)
+    assert fa.fa_std_workspace_bytes(2, 3, 100, 64) == 2 * 3 * 100 * 100 * 2
+    assert fa.fa_std_workspace_bytes(1, 32, 32768, 128) == 32 * 32768 * 32768 * 2  # > 2^32
+    assert fa.fa_std_workspace_bytes(0, 1, 16, 64) == 0
+    assert fa.fa_std_workspace_bytes(1, 1, 16, 96) == 0
+
+
+def test_std_validation(lib):
+    B, H, N, d = 1, 2, 64, 64
+    need = fa.fa_std_workspace_bytes(B, H, N, d)
+
+    def std(**kw):
+        a = dict(dtype=fa.FA_BF16, q=FAKE, ws=ctypes.c_void_p(0x10000), wsb=need, B=B, H=H,
+                 d=d, scale=0.1)
+        a.update(kw)
+        return lib.fa_std_fwd(a["dtype"], a["q"], FAKE, FAKE, FAKE, a["ws"], a["wsb"], a["B"],
+                              a["H"], N, a["d"], a["scale"], 0, None)
+
+    assert std(q=None) == -1
+    assert std(ws=None) == -1
+    assert std(dtype=fa.FA_F32) == -3
+    assert std(dtype=7) == -3
+    assert std(d=32) == -4
+    assert std(B=0) == -2
+    assert std(B=256, H=256) == -2  # B*H beyond the score pass's grid limit
+    assert std(wsb=need - 1) == -5
+    assert std(ws=ctypes.c_void_p(0x10010)) == -5
+    assert std(scale=float("inf")) == -7
+
+
+def test_library_has_no_unresolved_kernel_stubs():
+    # A kernel whose host-side launch stub was not emitted shows up as an
+    # undefined __device_stub__ symbol and makes dlopen fail on first use.
+    import subprocess
+    out = subprocess.run(["nm", "-D", fa.LIB_PATH], capture_output=True, text=True).stdout
+    missing = [ln for ln in out.splitlines() if " U " in ln and "__device_stub__" in ln]
+    assert missing == []
