@@ -14,8 +14,10 @@ recurrence the kernels use.
 Modules
 -------
 attention
-    Forward (O and per-row logsumexp) and backward (dQ, dK, dV) from the
-    plain definition. Pinned by tests/test_oracle.py.
+    Forward (O and per-row logsumexp, also with fewer queries than keys) and
+    backward (dQ, dK, dV) from the plain definition, and the merge of results
+    over disjoint key sets. Pinned by tests/test_oracle.py and
+    tests/test_oracle_splitkv.py.
 online
     The blocked online-softmax recurrence of the pages' tiling algorithm, in
     both loop orders. Used only to pin the exactness of the oracle.
@@ -34,6 +36,7 @@ from .attention import (  # noqa: F401
     attention_backward,
     attention_forward_rows,
     counted_flops,
+    merge_partials,
 )
 from .e4m3 import e4m3_decode, e4m3_encode, E4M3_MAX  # noqa: F401
 from .online import online_forward_kv_outer, online_forward_q_outer  # noqa: F401

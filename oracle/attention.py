@@ -69,11 +69,15 @@ def _row_chunk(n, chunk_elems):
     return max(1, min(n, chunk_elems // max(n, 1)))
 
 
-def attention_forward(q, k, v, scale, causal, chunk_elems=_DEFAULT_CHUNK_ELEMS):
+def attention_forward(q, k, v, scale, causal, chunk_elems=_DEFAULT_CHUNK_ELEMS, q_offset=0):
     """O = softmax(scale q k^T [masked]) v and LSE_i = m_i + ln l_i.
 
-    Inputs ``[..., N, d]``; returns O ``[..., N, d]`` and LSE ``[..., N]``
-    (float64).
+    Inputs ``[..., N, d]`` (queries) and ``[..., Nk, d]`` (keys, values; Nk may
+    differ from N); returns O ``[..., N, d]`` and LSE ``[..., N]`` (float64).
+    ``q_offset`` is the position of the first query in the key sequence: with
+    ``causal`` query i sees keys 0 .. q_offset + i. With N queries taken as the
+    last N of Nk positions (decoding), q_offset = Nk - N; a row that sees no
+    key at all gets O = 0 and LSE = -inf.
     """
     qh, lead = _heads(q)
     kh, _ = _heads(k)
@@ -86,11 +90,40 @@ def attention_forward(q, k, v, scale, causal, chunk_elems=_DEFAULT_CHUNK_ELEMS):
     for h in range(nh):
         for r0 in range(0, n, rc):
             r1 = min(n, r0 + rc)
-            s = scores(qh[h, r0:r1], kh[h], scale, causal, row0=r0)
+            s = scores(qh[h, r0:r1], kh[h], scale, causal, row0=q_offset + r0)
+            empty = np.all(np.isneginf(s), axis=1)
+            if np.any(empty):
+                s = np.where(empty[:, None], 0.0, s)
             p, m, l = softmax_rows(s)
-            o[h, r0:r1] = p @ vh[h]
-            lse[h, r0:r1] = m + np.log(l)
+            o[h, r0:r1] = np.where(empty[:, None], 0.0, p @ vh[h])
+            lse[h, r0:r1] = np.where(empty, -np.inf, m + np.log(l))
     return o.reshape(lead + (n, dv)), lse.reshape(lead + (n,))
+
+
+def merge_partials(o_parts, lse_parts):
+    """Combine attention over disjoint key sets into attention over their union.
+
+    ``o_parts`` [P, ..., d] and ``lse_parts`` [P, ...] hold, for each part p,
+    the normalised output O_p = sum_j exp(S_j - LSE_p) V_j and LSE_p =
+    ln sum_j exp(S_j) over that part's keys. Over the union the softmax
+    denominator is the sum of the parts' denominators, so
+      LSE = ln sum_p exp(LSE_p),   O = sum_p exp(LSE_p - LSE) O_p
+    (the rescaling of partial results by exp(m_old - m_new) in "11.11 Flash
+    Attention", section "Flash Attention: The Key Insight", applied once to
+    whole parts). Parts with LSE_p = -inf (no visible key) contribute
+    nothing; if every part is empty the result is O = 0, LSE = -inf.
+    """
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    m = np.max(lse_parts, axis=0)
+    m_safe = np.where(np.isneginf(m), 0.0, m)
+    w = np.exp(lse_parts - m_safe[None])                # 0 for empty parts
+    tot = np.sum(w, axis=0)
+    lse = np.where(tot > 0, m_safe + np.log(np.where(tot > 0, tot, 1.0)), -np.inf)
+    coef = np.where(tot[None] > 0, w / np.where(tot > 0, tot, 1.0)[None], 0.0)
+    # an empty part's O is never read (its weight is exactly 0)
+    o = np.sum(np.where(coef[..., None] > 0, coef[..., None] * o_parts, 0.0), axis=0)
+    return o, lse
 
 
 def attention_forward_rows(q, k, v, rows, scale, causal):
