@@ -16,6 +16,9 @@ Prints ONE JSON line on stdout. Besides the contract fields it carries
   breakdown    -- per-launch times and TFLOPS.
 `--suite PATH` additionally times every workload of the parity suite and
 writes one JSON line per workload to PATH.
+`--decode PATH` runs only the split-KV (few queries, many keys) workloads and
+writes one JSON line per workload (median of 20 after 5 warm-ups; HBM rate
+from the bytes of Q, K, V and O read or written once).
 `--compare-standard PATH` runs only the comparison of the IO-aware forward with
 the standard (materialising) forward that the pages' exercise describes
 (B=1, H=32, d=128, fp16 random normals, N = 2048, 8192, 32768; 3 warm-up and
@@ -323,6 +326,50 @@ def run_compare(path, torch, fa, inputs, lengths=(2048, 8192, 32768)):
     out.close()
 
 
+DECODE_CASES = [
+    # (name, B, H, Nq, Nk, d, causal, seed)
+    ("decode bf16 B8 H32 Nq1 Nk32768 d128", 8, 32, 1, 32768, 128, False, 1031),
+    ("decode bf16 B1 H32 Nq1 Nk131072 d128", 1, 32, 1, 131072, 128, False, 1032),
+    ("chunk bf16 causal B8 H32 Nq16 Nk8192 d128", 8, 32, 16, 8192, 128, True, 1033),
+]
+
+
+def run_decode(path, torch, fa, inputs):
+    """Split-KV forward on decoding-shaped workloads: time and HBM rate."""
+    import statistics
+    out = open(path, "w")
+    for name, B, H, Nq, Nk, d, causal, seed in DECODE_CASES:
+        print(f"[decode] {name}", file=sys.stderr, flush=True)
+        q, k, v = inputs.draw_qkv_rect_device(B, H, Nq, Nk, d, seed, torch.bfloat16)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, Nq), device="cuda", dtype=torch.float32)
+        ws = torch.empty(fa.fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, 0), device="cuda",
+                         dtype=torch.uint8)
+        fn = lambda: fa.fa_fwd_splitkv(q, k, v, o, lse, ws, d ** -0.5, causal, 0)  # noqa: E731
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(20):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        med = statistics.median(times)
+        nbytes = 2 * (2 * B * H * Nq * d + 2 * B * H * Nk * d) + 4 * B * H * Nq
+        rec = {"workload": name, "median_ms": round(med, 4), "min_ms": round(min(times), 4),
+               "hbm_gbs": round(nbytes / (med * 1e-3) / 1e9, 1),
+               "frac_hbm": round(nbytes / (med * 1e-3) / 8.0e12, 4),
+               "algorithmic_bytes": nbytes, "seed": seed}
+        print(json.dumps(rec), file=out, flush=True)
+        print(f"[decode] {json.dumps(rec)}", file=sys.stderr, flush=True)
+        del q, k, v, o, lse, ws, fn
+        torch.cuda.empty_cache()
+    out.close()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -332,6 +379,8 @@ def main():
                     help="budget for the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--suite", metavar="PATH", help="also time every workload, JSON lines to PATH")
+    ap.add_argument("--decode", metavar="PATH",
+                    help="only run the split-KV decoding workloads, JSON lines to PATH")
     ap.add_argument("--compare-standard", metavar="PATH",
                     help="only run the IO-aware vs standard forward comparison, JSON lines to PATH")
     ap.add_argument("--compare-n", type=int, nargs="+", default=[2048, 8192, 32768],
@@ -346,14 +395,17 @@ def main():
               "communication, so the whole-job rate at N GPUs is N times the 1-GPU figure at "
               "the per-GPU head count; run with --gpus 1.", file=sys.stderr, flush=True)
         sys.exit(2)
-    if args.compare_standard:
+    if args.decode or args.compare_standard:
         import torch
         import exact_io_aware_54_amd as fa
         from exact_io_aware_54_amd import inputs
         if not torch.cuda.is_available():
             sys.exit("bench.py needs a GPU")
         fa.load_library()
-        run_compare(args.compare_standard, torch, fa, inputs, args.compare_n)
+        if args.decode:
+            run_decode(args.decode, torch, fa, inputs)
+        if args.compare_standard:
+            run_compare(args.compare_standard, torch, fa, inputs, args.compare_n)
         return
     run_main(args)
 

@@ -9,10 +9,11 @@ in the library's kernels; there is no fallback path. If the library has not
 been built, calls raise ``RuntimeError``.
 
 Entry points: ``fa_fwd``, ``fa_fwd_fp8``, ``fa_bwd``, ``fa_bwd_stage``,
-``fa_bwd_workspace_bytes``, ``fa_std_fwd``, ``fa_std_workspace_bytes``,
-``fa_status_string``, ``fa_version``; ``forward`` / ``backward`` /
-``forward_fp8`` / ``forward_standard`` allocate outputs with torch and call
-them.
+``fa_bwd_workspace_bytes``, ``fa_fwd_splitkv``,
+``fa_fwd_splitkv_workspace_bytes``, ``fa_lse_merge``, ``fa_std_fwd``,
+``fa_std_workspace_bytes``, ``fa_status_string``, ``fa_version``;
+``forward`` / ``backward`` / ``forward_fp8`` / ``forward_splitkv`` /
+``forward_standard`` allocate outputs with torch and call them.
 """
 
 import ctypes
@@ -58,6 +59,12 @@ def load_library(path=None):
     lib.fa_bwd.restype = i
     lib.fa_bwd_stage.argtypes = [i] + lib.fa_bwd.argtypes
     lib.fa_bwd_stage.restype = i
+    lib.fa_fwd_splitkv_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.fa_fwd_splitkv_workspace_bytes.restype = sz
+    lib.fa_fwd_splitkv.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
+    lib.fa_fwd_splitkv.restype = i
+    lib.fa_lse_merge.argtypes = [i, i, vp, vp, vp, vp, i, i, vp]
+    lib.fa_lse_merge.restype = i
     lib.fa_std_workspace_bytes.argtypes = [i, i, i, i]
     lib.fa_std_workspace_bytes.restype = sz
     lib.fa_std_fwd.argtypes = [i, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, vp]
@@ -184,6 +191,53 @@ def fa_bwd_stage(stage, q, k, v, o, lse, do, dq, dk, dv, workspace, scale, causa
     _raise("fa_bwd_stage", st)
 
 
+def fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, num_splits=0):
+    return int(load_library().fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, num_splits))
+
+
+def fa_fwd_splitkv(q, k, v, o, lse, workspace, scale, causal, num_splits=0, stream=None):
+    """Split-KV forward: q, o [B,H,Nq,d]; k, v [B,H,Nk,d]; lse [B,H,Nq] or None."""
+    import torch
+    lib = load_library()
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    _check_bhnd("q", q, (B, H, Nq, d), q.dtype)
+    _check_bhnd("o", o, (B, H, Nq, d), q.dtype)
+    _check_bhnd("k", k, (B, H, Nk, d), q.dtype)
+    _check_bhnd("v", v, (B, H, Nk, d), q.dtype)
+    if lse is not None:
+        _check_bhnd("lse", lse, (B, H, Nq), torch.float32)
+    if workspace.dtype != torch.uint8 or not workspace.is_cuda:
+        raise TypeError("workspace must be a uint8 device tensor")
+    st = lib.fa_fwd_splitkv(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                            None if lse is None else _ptr(lse), B, H, Nq, Nk, d, float(scale),
+                            int(bool(causal)), int(num_splits), _ptr(workspace),
+                            workspace.numel(), _stream(stream))
+    _raise("fa_fwd_splitkv", st)
+
+
+def fa_lse_merge(o_parts, lse_parts, o, lse=None, stream=None):
+    """Merge float32 parts o_parts [P, ..., d], lse_parts [P, ...] into o [..., d] (and lse)."""
+    import torch
+    lib = load_library()
+    P, d = o_parts.shape[0], o_parts.shape[-1]
+    rows = o_parts[0].numel() // d
+    if o_parts.dtype != torch.float32 or lse_parts.dtype != torch.float32:
+        raise TypeError("o_parts and lse_parts must be float32")
+    if tuple(lse_parts.shape) != tuple(o_parts.shape[:-1]):
+        raise ValueError("lse_parts must have the shape of o_parts without its last dim")
+    if tuple(o.shape) != tuple(o_parts.shape[1:]):
+        raise ValueError("o must have the shape of one part")
+    for name, t in (("o_parts", o_parts), ("lse_parts", lse_parts), ("o", o)):
+        if not (t.is_cuda and t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if lse is not None and (lse.dtype != torch.float32 or lse.numel() != rows or not lse.is_cuda):
+        raise ValueError("lse must be a float32 device tensor with one value per row")
+    st = lib.fa_lse_merge(_dtype_code(o), P, _ptr(o_parts), _ptr(lse_parts), _ptr(o),
+                          None if lse is None else _ptr(lse), rows, d, _stream(stream))
+    _raise("fa_lse_merge", st)
+
+
 def fa_std_workspace_bytes(B, H, N, d):
     return int(load_library().fa_std_workspace_bytes(B, H, N, d))
 
@@ -212,6 +266,20 @@ def forward(q, k, v, scale=None, causal=False):
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:-1], device=q.device, dtype=torch.float32)
     fa_fwd(q, k, v, o, lse, scale, causal)
+    return o, lse
+
+
+def forward_splitkv(q, k, v, scale=None, causal=False, num_splits=0):
+    """Allocate O, LSE and the workspace with torch and run fa_fwd_splitkv."""
+    import torch
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    scale = d ** -0.5 if scale is None else scale
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), device=q.device, dtype=torch.float32)
+    ws = torch.empty(max(1, fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, num_splits)),
+                     device=q.device, dtype=torch.uint8)
+    fa_fwd_splitkv(q, k, v, o, lse, ws, scale, causal, num_splits)
     return o, lse
 
 

@@ -27,6 +27,32 @@ int status_of(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Key ranges of fa_fwd_splitkv: whole 128-key tiles, as evenly as possible.
+// num_splits = 0 picks enough ranges for about two workgroups per CU.
+struct SplitPlan {
+    int splits;  // ranges actually used
+    int kps;     // keys per range (a multiple of 128)
+};
+
+int splitkv_shape(int B, int H, int Nq, int Nk, int d, int num_splits) {
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+    const int64_t bh = (int64_t)B * H;
+    if (bh * Nq * d >= ((int64_t)1 << 31) || bh * Nk * d >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
+    if (num_splits < 0 || num_splits > 1024) return FA_ERR_ARG;
+    return FA_OK;
+}
+
+SplitPlan splitkv_plan(int B, int H, int Nq, int Nk, int num_splits) {
+    const int tiles = (Nk + 127) / 128;
+    const int64_t units = (int64_t)B * H * ((Nq + 31) / 32);
+    int want = num_splits;
+    if (want == 0) want = (int)((512 + units - 1) / units);
+    want = want < 1 ? 1 : (want > tiles ? tiles : want);
+    const int tps = (tiles + want - 1) / want;
+    return SplitPlan{(tiles + tps - 1) / tps, tps * 128};
+}
+
 }  // namespace
 
 extern "C" {
@@ -42,7 +68,7 @@ const char* fa_status_string(int status) {
         case FA_ERR_HEADDIM: return "head dim not supported";
         case FA_ERR_WORKSPACE: return "workspace too small";
         case FA_ERR_HIP: return "HIP runtime error at launch";
-        case FA_ERR_ARG: return "invalid scalar argument (scale or descale)";
+        case FA_ERR_ARG: return "invalid scalar argument (scale, descale, split count) or misaligned pointer";
         default: return "unknown status";
     }
 }
@@ -122,6 +148,48 @@ int fa_bwd_stage(int stage, int dtype, const void* q, const void* k, const void*
     if (stage < 1 || stage > 3) return FA_ERR_ARG;
     return bwd_common(dtype, q, k, v, o, lse, dO, dq, dk, dv, workspace, workspace_bytes, B, H, N,
                       d, scale, causal, 1 << (stage - 1), stream);
+}
+
+size_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits) {
+    if (splitkv_shape(B, H, Nq, Nk, d, num_splits) != FA_OK) return 0;
+    const SplitPlan pl = splitkv_plan(B, H, Nq, Nk, num_splits);
+    const size_t rows = (size_t)pl.splits * B * H * Nq;
+    return align256(rows * d * sizeof(float)) + align256(rows * sizeof(float));
+}
+
+int fa_fwd_splitkv(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int Nq, int Nk, int d, float scale, int causal, int num_splits,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!q || !k || !v || !o || !workspace) return FA_ERR_NULL;
+    if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+    const int st = splitkv_shape(B, H, Nq, Nk, d, num_splits);
+    if (st != FA_OK) return st;
+    if (causal && Nq > Nk) return FA_ERR_SHAPE;
+    if (!good_scale(scale)) return FA_ERR_ARG;
+    if (workspace_bytes < fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, num_splits))
+        return FA_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255) != 0) return FA_ERR_WORKSPACE;
+    const SplitPlan pl = splitkv_plan(B, H, Nq, Nk, num_splits);
+    const int BH = B * H;
+    if ((int64_t)BH * ((Nq + 31) / 32) * pl.splits >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
+    const size_t rows = (size_t)pl.splits * BH * Nq;
+    float* o_part = static_cast<float*>(workspace);
+    float* lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                               align256(rows * d * sizeof(float)));
+    return status_of(fa::launch_fwd_splitkv(dtype, d, causal != 0, q, k, v, o, lse, o_part,
+                                            lse_part, BH, Nq, Nk, pl.splits, pl.kps, scale,
+                                            stream));
+}
+
+int fa_lse_merge(int dtype_out, int num_parts, const float* o_parts, const float* lse_parts,
+                 void* o, float* lse, int rows, int d, hipStream_t stream) {
+    if (!o_parts || !lse_parts || !o) return FA_ERR_NULL;
+    if (dtype_out != FA_F32 && dtype_out != FA_F16 && dtype_out != FA_BF16) return FA_ERR_DTYPE;
+    if (num_parts < 1 || rows < 1 || d < 4 || d % 4 != 0 || d > 65536) return FA_ERR_SHAPE;
+    if ((int64_t)rows * (d / 4) >= ((int64_t)1 << 38)) return FA_ERR_SHAPE;
+    if (((uintptr_t)o_parts & 15) != 0) return FA_ERR_ARG;
+    return status_of(fa::launch_lse_merge(dtype_out, o_parts, lse_parts, num_parts, rows, d, o, lse,
+                                          stream));
 }
 
 size_t fa_std_workspace_bytes(int B, int H, int N, int d) {

@@ -19,6 +19,12 @@ hipError_t launch_bwd(int dtype, int d, bool causal, const void* q, const void* 
                       const void* o, const float* lse, const void* dO, void* dq, void* dk,
                       void* dv, float* delta, float* lse2, int BH, int N, float scale,
                       int stages, hipStream_t stream);  // stages: bit 0 pre, 1 dK/dV, 2 dQ
+hipError_t launch_fwd_splitkv(int dtype, int d, bool causal, const void* q, const void* k,
+                              const void* v, void* o, float* lse, float* o_part, float* lse_part,
+                              int BH, int Nq, int Nk, int splits, int kps, float scale,
+                              hipStream_t stream);
+hipError_t launch_lse_merge(int dtype_out, const float* o_parts, const float* lse_parts, int P,
+                            long long rows, int d, void* o, float* lse, hipStream_t stream);
 hipError_t launch_std(int dtype, int d, bool causal, const void* q, const void* k, const void* v,
                       void* o, void* s, int BH, int N, float scale, hipStream_t stream);
 

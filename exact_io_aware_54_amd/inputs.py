@@ -24,6 +24,7 @@ SEEDS = {
     "causal_16k": 1013,
     "train_4k": 1004,
     "fp8_8k": 1005,
+    "decode_16k": 1021,   # split-KV parity: B4 H16 Nq1 Nk16384 d128
 }
 
 E4M3_MAX = 448.0
@@ -38,6 +39,34 @@ def draw_qkv(b, h, n, d, seed, dtype=torch.float32, with_do=False):
     if with_do:
         out.append(torch.randn(shape, generator=g, dtype=torch.float32))
     return tuple(t.to(dtype).contiguous() for t in out)
+
+
+def draw_qkv_rect(b, h, nq, nk, d, seed, dtype=torch.float32):
+    """Return (q [b,h,nq,d], k [b,h,nk,d], v [b,h,nk,d]) CPU tensors in ``dtype``.
+
+    Same recipe as draw_qkv (float32 N(0, 1), drawn in the order Q, K, V) with
+    fewer queries than keys, for the split-KV (decoding) workloads.
+    """
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    q = torch.randn((b, h, nq, d), generator=g, dtype=torch.float32)
+    k = torch.randn((b, h, nk, d), generator=g, dtype=torch.float32)
+    v = torch.randn((b, h, nk, d), generator=g, dtype=torch.float32)
+    return tuple(t.to(dtype).contiguous() for t in (q, k, v))
+
+
+def draw_qkv_rect_device(b, h, nq, nk, d, seed, dtype, device="cuda"):
+    """Like draw_qkv_rect, but drawn by torch's generator on ``device``.
+
+    For timing-only workloads too large to draw on the host (the values differ
+    from the CPU draw of the same seed; parity tests use draw_qkv_rect).
+    """
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    q = torch.randn((b, h, nq, d), generator=g, device=device, dtype=torch.float32).to(dtype)
+    k = torch.randn((b, h, nk, d), generator=g, device=device, dtype=torch.float32).to(dtype)
+    v = torch.randn((b, h, nk, d), generator=g, device=device, dtype=torch.float32).to(dtype)
+    return q, k, v
 
 
 def draw_fp8(b, h, n, d, seed, outlier_p=0.01, outlier_mul=20.0):

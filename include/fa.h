@@ -59,7 +59,8 @@ typedef enum {
     FA_ERR_WORKSPACE = -5,  /* workspace too small or not 256-byte aligned      */
     FA_ERR_HIP = -6,        /* the HIP runtime reported an error at launch       */
     FA_ERR_ARG = -7         /* a scalar argument is invalid (scale not finite or
-                               not positive, descale not finite or <= 0)         */
+                               not positive, descale not finite or <= 0, split
+                               count out of range) or a pointer is misaligned    */
 } fa_status;
 
 /*
@@ -135,6 +136,55 @@ int fa_bwd_stage(int stage, int dtype, const void* q, const void* k, const void*
                  const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv,
                  void* workspace, size_t workspace_bytes,
                  int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/*
+ * Size in bytes of the scratch buffer fa_fwd_splitkv needs for these
+ * arguments (same num_splits): the partial outputs (float32,
+ * splits x B x H x Nq x d) and partial LSE values of every key range.
+ * Returns 0 for invalid arguments.
+ */
+size_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits);
+
+/*
+ * Forward pass for few queries over many keys (decoding, chunked prefill):
+ * the keys are cut into ranges, every (batch, head, 32 queries, key range)
+ * is an independent workgroup that writes a normalised partial output and its
+ * LSE, and the parts are merged as in fa_lse_merge. Same O and LSE as the
+ * definition ("11.11 Flash Attention", section "Flash Attention: The Key
+ * Insight": partial softmax results are combined by rescaling with the
+ * exponential of the difference of their maxima).
+ *   dtype      FA_BF16 or FA_F16.
+ *   q, o       [B,H,Nq,d] of `dtype`;  k, v [B,H,Nk,d] of `dtype`.
+ *   lse        [B,H,Nq] float32, written; may be NULL.
+ *   causal     the queries are the last Nq positions of the Nk keys: query i
+ *              sees keys 0 .. Nk - Nq + i (needs Nq <= Nk, else
+ *              FA_ERR_SHAPE); Nq = Nk is the square causal mask.
+ *   num_splits number of key ranges (1..1024; capped at ceil(Nk / 128)), or
+ *              0 to let the library choose about two workgroups per CU.
+ *   workspace  at least fa_fwd_splitkv_workspace_bytes(...) bytes, 256-byte
+ *              aligned; overwritten.
+ * Nq and Nk are any positive sizes with B*H*max(Nq,Nk)*d < 2^31.
+ */
+int fa_fwd_splitkv(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int Nq, int Nk, int d, float scale, int causal, int num_splits,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Merge of attention results over disjoint key sets (the step that joins
+ * split key ranges, or the shards of a sequence split across devices): with
+ * part p's normalised output O_p and LSE_p = ln sum_{j in part} exp(S_j),
+ *   LSE = ln sum_p exp(LSE_p),   O = sum_p exp(LSE_p - LSE) O_p
+ * ("11.11 Flash Attention", section "Flash Attention: The Key Insight").
+ * A part with LSE_p = -inf has no visible key and is skipped (its O_p is not
+ * read); a row whose parts are all empty gets O = 0 and LSE = -inf.
+ *   dtype_out  type of o: FA_F32, FA_F16 or FA_BF16.
+ *   o_parts    [num_parts][rows][d] float32, 16-byte aligned (FA_ERR_ARG if not).
+ *   lse_parts  [num_parts][rows] float32.
+ *   o          [rows][d] of dtype_out, written;  lse [rows] float32 or NULL.
+ *   d          a multiple of 4 (FA_ERR_SHAPE otherwise).
+ */
+int fa_lse_merge(int dtype_out, int num_parts, const float* o_parts, const float* lse_parts,
+                 void* o, float* lse, int rows, int d, hipStream_t stream);
 
 /*
  * Size in bytes of the scratch buffer fa_std_fwd needs: the N x N score

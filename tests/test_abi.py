@@ -157,3 +157,59 @@ def test_library_has_no_unresolved_kernel_stubs():
     out = subprocess.run(["nm", "-D", fa.LIB_PATH], capture_output=True, text=True).stdout
     missing = [ln for ln in out.splitlines() if " U " in ln and "__device_stub__" in ln]
     assert missing == []
+
+
+def test_splitkv_workspace_bytes(lib):
+    # 8 tiles of 128 keys, 4 requested ranges -> 4 ranges of 2 tiles;
+    # partial O: 4 * (1*2*3) rows * 64 floats, partial LSE: 24 floats (each padded to 256 B)
+    assert fa.fa_fwd_splitkv_workspace_bytes(1, 2, 3, 1000, 64, 4) == 6144 + 256
+    # automatic: 2 (batch*head*query-block) units -> 256 wanted, capped at the 8 tiles
+    assert fa.fa_fwd_splitkv_workspace_bytes(1, 2, 3, 1000, 64, 0) == 12288 + 256
+    # 7 requested of 8 tiles -> 2 tiles per range -> 4 ranges
+    assert fa.fa_fwd_splitkv_workspace_bytes(1, 2, 3, 1000, 64, 7) == 6144 + 256
+    assert fa.fa_fwd_splitkv_workspace_bytes(1, 2, 3, 1000, 80, 1) == 0
+    assert fa.fa_fwd_splitkv_workspace_bytes(1, 2, 3, 1000, 64, -1) == 0
+
+
+def test_splitkv_validation(lib):
+    B, H, Nq, Nk, d = 1, 2, 4, 300, 64
+    need = fa.fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, 2)
+
+    def skv(**kw):
+        a = dict(dtype=fa.FA_BF16, q=FAKE, Nq=Nq, Nk=Nk, d=d, scale=0.1, causal=0, ns=2,
+                 ws=ctypes.c_void_p(0x10000), wsb=need)
+        a.update(kw)
+        return lib.fa_fwd_splitkv(a["dtype"], a["q"], FAKE, FAKE, FAKE, None, B, H, a["Nq"],
+                                  a["Nk"], a["d"], a["scale"], a["causal"], a["ns"], a["ws"],
+                                  a["wsb"], None)
+
+    assert skv(q=None) == -1
+    assert skv(ws=None) == -1
+    assert skv(dtype=fa.FA_F32) == -3
+    assert skv(d=96) == -4
+    assert skv(Nq=0) == -2
+    assert skv(Nk=0) == -2
+    assert skv(causal=1, Nq=400) == -2       # causal needs Nq <= Nk
+    assert skv(ns=-1) == -7
+    assert skv(ns=1025) == -7
+    assert skv(scale=-1.0) == -7
+    assert skv(wsb=need - 1) == -5
+    assert skv(ws=ctypes.c_void_p(0x10008)) == -5
+
+
+def test_lse_merge_validation(lib):
+    def merge(**kw):
+        a = dict(dt=fa.FA_F32, P=2, op=ctypes.c_void_p(0x10000), lp=FAKE, o=FAKE, rows=10, d=64)
+        a.update(kw)
+        return lib.fa_lse_merge(a["dt"], a["P"], a["op"], a["lp"], a["o"], None, a["rows"],
+                                a["d"], None)
+
+    assert merge(op=None) == -1
+    assert merge(lp=None) == -1
+    assert merge(o=None) == -1
+    assert merge(dt=9) == -3
+    assert merge(P=0) == -2
+    assert merge(rows=0) == -2
+    assert merge(d=6) == -2
+    assert merge(d=0) == -2
+    assert merge(op=ctypes.c_void_p(0x10004)) == -7  # o_parts not 16-byte aligned
