@@ -218,6 +218,8 @@ def run_suite(path, torch, fa, inputs):
          "causal_16k"),
         ("fwd bf16 causal B8 H16 N4096 d128", "fwd", torch.bfloat16, 8, 16, 4096, 128, True,
          "train_4k"),
+        ("fwd bf16 causal B1 H32 N8192 d256", "fwd", torch.bfloat16, 1, 32, 8192, 256, True,
+         "causal_8k"),
         ("bwd bf16 causal B8 H16 N4096 d128", "bwd", torch.bfloat16, 8, 16, 4096, 128, True,
          "train_4k"),
         ("fwd fp8 B2 H32 N8192 d128", "fp8", None, 2, 32, 8192, 128, False, "fp8_8k"),

@@ -13,9 +13,11 @@ namespace {
 
 constexpr int kVersion = 100;  // 0.1.0
 
-int check_shape(int B, int H, int N, int d) {
+// Shape checks shared by the entry points; head dims 64 and 128 everywhere,
+// 256 only where the caller allows it (the 16-bit forward).
+int check_shape(int B, int H, int N, int d, bool allow256 = false) {
     if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
-    if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+    if (d != 64 && d != 128 && !(allow256 && d == 256)) return FA_ERR_HEADDIM;
     const int64_t total = (int64_t)B * H * N * d;
     if (total >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
     return FA_OK;
@@ -77,7 +79,7 @@ int fa_fwd(int dtype, const void* q, const void* k, const void* v, void* o, floa
            int H, int N, int d, float scale, int causal, hipStream_t stream) {
     if (!q || !k || !v || !o) return FA_ERR_NULL;
     if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
-    const int st = check_shape(B, H, N, d);
+    const int st = check_shape(B, H, N, d, dtype != FA_F32);
     if (st != FA_OK) return st;
     if (!good_scale(scale)) return FA_ERR_ARG;
     const int BH = B * H;

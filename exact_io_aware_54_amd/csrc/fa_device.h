@@ -98,11 +98,14 @@ __device__ __forceinline__ int acc_kperm16(int kk) {
 //  * ds_read_b64_tr_b16: 4 consecutive rows (first one a multiple of 4),
 //    4 consecutive chunks each (chunk index a multiple of 4 first).
 // D = 128 (one row per 256 bytes of banks): swap the two 2-bit halves of r%16.
+// D = 256 (one row per 512 bytes): chunk c of every row falls on the banks of
+// chunk c % 16, so the D = 128 pattern, applied to the low four bits of the
+// chunk index, keeps both read patterns conflict-free.
 // D = 64 (two rows per 256 bytes): g = (r/2)%8, rotate its 3 bits right by 1.
 template <int D>
 __device__ __forceinline__ int tile_swz(int r) {
-    static_assert(D == 64 || D == 128, "head dim 64 or 128");
-    if constexpr (D == 128) {
+    static_assert(D == 64 || D == 128 || D == 256, "head dim 64, 128 or 256");
+    if constexpr (D >= 128) {
         return ((r & 3) << 2) | ((r >> 2) & 3);
     } else {
         const int g = (r >> 1) & 7;

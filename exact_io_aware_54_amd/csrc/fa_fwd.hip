@@ -243,7 +243,7 @@ struct FwdWave {
 };
 
 template <typename T, int D, bool CAUSAL, int NW>
-__global__ void __launch_bounds__(64 * NW, 2)
+__global__ void __launch_bounds__(64 * NW, D > 128 ? 1 : 2)
 fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
                 T* __restrict__ O, float* __restrict__ LSE, int BH, int N, int nqb, float c) {
     using C = FwdTile<D, NW>;
@@ -295,12 +295,18 @@ hipError_t launch_typed(const void* q, const void* k, const void* v, void* o, fl
     return launch_nw<T, D, CAUSAL, 8>(q, k, v, o, lse, BH, N, scale, stream);
 }
 
+// Head dim 256: the Q operand and the output accumulators need about 470
+// registers per wave, so one wave per SIMD (four per workgroup), with the
+// accumulators in AGPRs.
 template <typename T>
 hipError_t launch_d(int d, bool causal, const void* q, const void* k, const void* v, void* o,
                     float* lse, int BH, int N, float scale, hipStream_t stream) {
     if (d == 64)
         return causal ? launch_typed<T, 64, true>(q, k, v, o, lse, BH, N, scale, stream)
                       : launch_typed<T, 64, false>(q, k, v, o, lse, BH, N, scale, stream);
+    if (d == 256)
+        return causal ? launch_nw<T, 256, true, 4>(q, k, v, o, lse, BH, N, scale, stream)
+                      : launch_nw<T, 256, false, 4>(q, k, v, o, lse, BH, N, scale, stream);
     return causal ? launch_typed<T, 128, true>(q, k, v, o, lse, BH, N, scale, stream)
                   : launch_typed<T, 128, false>(q, k, v, o, lse, BH, N, scale, stream);
 }

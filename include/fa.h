@@ -24,7 +24,8 @@
  *    caller. The library allocates no memory and keeps no per-call state.
  *  - Layout: contiguous row-major [B, H, N, d] for Q, K, V, O, dO, dQ, dK, dV;
  *    LSE is [B, H, N] float32 (natural log, of the scaled scores).
- *  - d must be 64 or 128. B, H, N >= 1 and B*H*N*d < 2^31.
+ *  - d must be 64 or 128 (the 16-bit fa_fwd also takes 256). B, H, N >= 1
+ *    and B*H*N*d < 2^31.
  *  - causal != 0: query i attends to keys 0..i (the mask is not on the pages;
  *    it is the usual lower-triangular mask with N_q = N_k).
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
@@ -55,7 +56,7 @@ typedef enum {
     FA_ERR_NULL = -1,       /* a required pointer is NULL                      */
     FA_ERR_SHAPE = -2,      /* B, H or N < 1, or the tensor is too large         */
     FA_ERR_DTYPE = -3,      /* dtype not supported by this entry point           */
-    FA_ERR_HEADDIM = -4,    /* d not in {64, 128}                                */
+    FA_ERR_HEADDIM = -4,    /* d not supported by this entry point               */
     FA_ERR_WORKSPACE = -5,  /* workspace too small or not 256-byte aligned      */
     FA_ERR_HIP = -6,        /* the HIP runtime reported an error at launch       */
     FA_ERR_ARG = -7         /* a scalar argument is invalid (scale not finite or
@@ -69,6 +70,7 @@ typedef enum {
  *          rounded to the input type before the P V product, O rounded to
  *          nearest even on store.
  *          FA_F32: float32 arithmetic throughout (no reduced-precision step).
+ *   d      64, 128, or (FA_BF16 / FA_F16 only) 256.
  *   q, k, v  [B,H,N,d] of `dtype`, read only.
  *   o        [B,H,N,d] of `dtype`, written.
  *   lse      [B,H,N] float32, written; may be NULL if not wanted.

@@ -73,7 +73,9 @@ def test_fwd_validation(lib):
     assert fwd(lib, B=0) == -2
     assert fwd(lib, N=-5) == -2
     assert fwd(lib, d=96) == -4
-    assert fwd(lib, d=256) == -4
+    assert fwd(lib, d=512) == -4
+    assert fwd(lib, dtype=fa.FA_F32, d=256) == -4   # 256 only on the 16-bit path
+    assert fwd(lib, d=256, B=1 << 14, H=1 << 10, N=1 << 10) == -2
     assert fwd(lib, B=1 << 14, H=1 << 10, N=1 << 10, d=128) == -2  # 2^41 elements
     assert fwd(lib, scale=0.0) == -7
     assert fwd(lib, scale=float("nan")) == -7
@@ -111,6 +113,7 @@ def test_bwd_validation(lib):
     assert bwd(ws=None) == -1
     assert bwd(dtype=fa.FA_F32) == -3
     assert bwd(d=80) == -4
+    assert bwd(d=256) == -4
     assert bwd(wsb=need - 1) == -5
     assert bwd(ws=ctypes.c_void_p(0x10010)) == -5  # not 256-byte aligned
     assert bwd(scale=0.0) == -7

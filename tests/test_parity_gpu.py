@@ -81,6 +81,35 @@ def test_fwd_16bit_small(gpu_lib, dtype, d, causal, N):
     assert max_abs(lse, l_ref) <= 1e-3
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 17, 64, 65, 300])
+def test_fwd_d256_small(gpu_lib, dtype, causal, N):
+    o, lse, o_ref, l_ref = check_fwd_full(gpu_lib, dtype, 1, 3, N, 256, causal, 3500 + N)
+    assert max_abs(o, o_ref) <= 2e-2
+    assert rel_frob(o, o_ref) <= 1e-2
+    assert max_abs(lse, l_ref) <= 1e-3
+
+
+def test_fwd_d256_workload(gpu_lib):
+    """Head dim 256 (the largest the pages' SDPA interface takes), causal, N = 4096."""
+    B, H, N, d = 1, 16, 4096, 256
+    note(f"fwd bf16 causal B{B} H{H} N{N} d{d}")
+    q, k, v = inputs.draw_qkv(B, H, N, d, 3601, torch.bfloat16)
+    o, lse = gpu_lib.forward(*dev(q, k, v), causal=True)
+    torch.cuda.synchronize()
+    o64, l64 = to64(o), to64(lse)
+    assert np.all(np.isfinite(o64)) and np.all(np.isfinite(l64))
+    rng = np.random.default_rng(3601)
+    for h in (0, 9, 15):
+        rows = _sample_rows(N, rng)
+        o_ref, l_ref = oracle.attention_forward_rows(to64(q[0, h]), to64(k[0, h]), to64(v[0, h]),
+                                                     rows, d ** -0.5, True)
+        assert max_abs(o64[0, h, rows], o_ref) <= 2e-2, h
+        assert rel_frob(o64[0, h, rows], o_ref) <= 1e-2, h
+        assert max_abs(l64[0, h, rows], l_ref) <= 1e-3, h
+
+
 def test_fwd_scale_argument(gpu_lib):
     """A scale other than 1/sqrt(d) reaches the scores (sharp softmax)."""
     o, lse, o_ref, l_ref = check_fwd_full(gpu_lib, "bf16", 1, 2, 200, 64, True, 3999, scale=0.9)
