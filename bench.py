@@ -19,6 +19,11 @@ writes one JSON line per workload to PATH.
 `--decode PATH` runs only the split-KV (few queries, many keys) workloads and
 writes one JSON line per workload (median of 20 after 5 warm-ups; HBM rate
 from the bytes of Q, K, V and O read or written once).
+`--loop-order PATH` runs only the loop-order ablation: the first-generation
+order (fa_fwd_v1: K/V blocks outer, one workgroup per head, O / m / l through
+memory) against the fused forward on the exercise shapes (B=1, H=32, d=128,
+fp16, N = 2048 and 8192, causal and not; and B=8 at N=2048, where the
+first-generation order has one workgroup per CU), one JSON line per case.
 `--compare-standard PATH` runs only the comparison of the IO-aware forward with
 the standard (materialising) forward that the pages' exercise describes
 (B=1, H=32, d=128, fp16 random normals, N = 2048, 8192, 32768; 3 warm-up and
@@ -372,6 +377,54 @@ def run_decode(path, torch, fa, inputs):
     out.close()
 
 
+def run_loop_order(path, torch, fa, inputs):
+    """First-generation loop order vs the fused (second-generation) forward."""
+    H, d = 32, 128
+    scale = d ** -0.5
+    out = open(path, "w")
+    # B = 8 gives the first-generation order one workgroup per CU (256 heads), so
+    # its gap to the fused kernel there is the loop order and round trips alone
+    for B, N, causal in ((1, 2048, False), (1, 2048, True), (1, 8192, False), (1, 8192, True),
+                         (8, 2048, False)):
+        seed = 1100 + N // 1024 + (B - 1)
+        print(f"[loop-order] N={N} causal={causal}", file=sys.stderr, flush=True)
+        q, k, v = (t.cuda() for t in inputs.draw_qkv(B, H, N, d, seed, torch.float16))
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), device="cuda", dtype=torch.float32)
+        ws = torch.empty(fa.fa_fwd_v1_workspace_bytes(B, H, N, d), device="cuda",
+                         dtype=torch.uint8)
+        fns = {"v1_kv_outer": lambda: fa.fa_fwd_v1(q, k, v, o, lse, ws, scale, causal),
+               "v2_fused": lambda: fa.fa_fwd(q, k, v, o, lse, scale, causal)}
+        rec = {"workload": f"fwd f16 B{B} H{H} N{N} d{d} causal={causal}", "seed": seed}
+        flops = counted_flops(B, H, N, d, causal)
+        for name, fn in fns.items():
+            reps = 3 if name == "v1_kv_outer" else 10
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            rec[name] = {"time_ms": round(ms, 3),
+                         "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
+        # O, m, l round trips of the first-generation order: per (K/V block of 64,
+        # Q block of 128) pair, O (fp32) and Q are read and O written
+        nkb, nqb = (N + 63) // 64, (N + 127) // 128
+        pairs = nkb * nqb if not causal else sum(
+            1 for j in range(nkb) for i in range(nqb) if j * 64 <= i * 128 + 127)
+        rec["v1_round_trip_bytes"] = B * H * pairs * 128 * d * (4 + 4 + 2)
+        rec["speedup_v2_over_v1"] = round(rec["v1_kv_outer"]["time_ms"] /
+                                          rec["v2_fused"]["time_ms"], 1)
+        print(json.dumps(rec), file=out, flush=True)
+        print(f"[loop-order] {json.dumps(rec)}", file=sys.stderr, flush=True)
+        del q, k, v, o, lse, ws, fns
+        torch.cuda.empty_cache()
+    out.close()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -381,6 +434,8 @@ def main():
                     help="budget for the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--suite", metavar="PATH", help="also time every workload, JSON lines to PATH")
+    ap.add_argument("--loop-order", metavar="PATH",
+                    help="only run the loop-order ablation, JSON lines to PATH")
     ap.add_argument("--decode", metavar="PATH",
                     help="only run the split-KV decoding workloads, JSON lines to PATH")
     ap.add_argument("--compare-standard", metavar="PATH",
@@ -397,7 +452,7 @@ def main():
               "communication, so the whole-job rate at N GPUs is N times the 1-GPU figure at "
               "the per-GPU head count; run with --gpus 1.", file=sys.stderr, flush=True)
         sys.exit(2)
-    if args.decode or args.compare_standard:
+    if args.decode or args.compare_standard or args.loop_order:
         import torch
         import exact_io_aware_54_amd as fa
         from exact_io_aware_54_amd import inputs
@@ -406,6 +461,8 @@ def main():
         fa.load_library()
         if args.decode:
             run_decode(args.decode, torch, fa, inputs)
+        if args.loop_order:
+            run_loop_order(args.loop_order, torch, fa, inputs)
         if args.compare_standard:
             run_compare(args.compare_standard, torch, fa, inputs, args.compare_n)
         return

@@ -10,10 +10,11 @@ been built, calls raise ``RuntimeError``.
 
 Entry points: ``fa_fwd``, ``fa_fwd_fp8``, ``fa_bwd``, ``fa_bwd_stage``,
 ``fa_bwd_workspace_bytes``, ``fa_fwd_splitkv``,
-``fa_fwd_splitkv_workspace_bytes``, ``fa_lse_merge``, ``fa_std_fwd``,
+``fa_fwd_splitkv_workspace_bytes``, ``fa_lse_merge``, ``fa_fwd_v1``,
+``fa_fwd_v1_workspace_bytes``, ``fa_std_fwd``,
 ``fa_std_workspace_bytes``, ``fa_status_string``, ``fa_version``;
 ``forward`` / ``backward`` / ``forward_fp8`` / ``forward_splitkv`` /
-``forward_standard`` allocate outputs with torch and call them.
+``forward_v1`` / ``forward_standard`` allocate outputs with torch and call them.
 """
 
 import ctypes
@@ -65,6 +66,10 @@ def load_library(path=None):
     lib.fa_fwd_splitkv.restype = i
     lib.fa_lse_merge.argtypes = [i, i, vp, vp, vp, vp, i, i, vp]
     lib.fa_lse_merge.restype = i
+    lib.fa_fwd_v1_workspace_bytes.argtypes = [i, i, i, i]
+    lib.fa_fwd_v1_workspace_bytes.restype = sz
+    lib.fa_fwd_v1.argtypes = [i, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, vp]
+    lib.fa_fwd_v1.restype = i
     lib.fa_std_workspace_bytes.argtypes = [i, i, i, i]
     lib.fa_std_workspace_bytes.restype = sz
     lib.fa_std_fwd.argtypes = [i, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, vp]
@@ -238,6 +243,27 @@ def fa_lse_merge(o_parts, lse_parts, o, lse=None, stream=None):
     _raise("fa_lse_merge", st)
 
 
+def fa_fwd_v1_workspace_bytes(B, H, N, d):
+    return int(load_library().fa_fwd_v1_workspace_bytes(B, H, N, d))
+
+
+def fa_fwd_v1(q, k, v, o, lse, workspace, scale, causal, stream=None):
+    """First-generation loop order (K/V blocks outer, O/m/l through memory)."""
+    import torch
+    lib = load_library()
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _check_bhnd(name, t, (B, H, N, d), q.dtype)
+    if lse is not None:
+        _check_bhnd("lse", lse, (B, H, N), torch.float32)
+    if workspace.dtype != torch.uint8 or not workspace.is_cuda:
+        raise TypeError("workspace must be a uint8 device tensor")
+    st = lib.fa_fwd_v1(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                       None if lse is None else _ptr(lse), _ptr(workspace), workspace.numel(),
+                       B, H, N, d, float(scale), int(bool(causal)), _stream(stream))
+    _raise("fa_fwd_v1", st)
+
+
 def fa_std_workspace_bytes(B, H, N, d):
     return int(load_library().fa_std_workspace_bytes(B, H, N, d))
 
@@ -280,6 +306,18 @@ def forward_splitkv(q, k, v, scale=None, causal=False, num_splits=0):
     ws = torch.empty(max(1, fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, num_splits)),
                      device=q.device, dtype=torch.uint8)
     fa_fwd_splitkv(q, k, v, o, lse, ws, scale, causal, num_splits)
+    return o, lse
+
+
+def forward_v1(q, k, v, scale=None, causal=False):
+    """Allocate O, LSE and the workspace with torch and run fa_fwd_v1."""
+    import torch
+    B, H, N, d = q.shape
+    scale = d ** -0.5 if scale is None else scale
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32)
+    ws = torch.empty(fa_fwd_v1_workspace_bytes(B, H, N, d), device=q.device, dtype=torch.uint8)
+    fa_fwd_v1(q, k, v, o, lse, ws, scale, causal)
     return o, lse
 
 

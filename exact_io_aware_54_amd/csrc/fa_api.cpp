@@ -194,6 +194,32 @@ int fa_lse_merge(int dtype_out, int num_parts, const float* o_parts, const float
                                           stream));
 }
 
+size_t fa_fwd_v1_workspace_bytes(int B, int H, int N, int d) {
+    if (check_shape(B, H, N, d) != FA_OK) return 0;
+    const size_t rows = (size_t)B * H * N;
+    return align256(rows * d * sizeof(float)) + 2 * align256(rows * 2 * sizeof(float));
+}
+
+int fa_fwd_v1(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+              void* workspace, size_t workspace_bytes, int B, int H, int N, int d, float scale,
+              int causal, hipStream_t stream) {
+    if (!q || !k || !v || !o || !workspace) return FA_ERR_NULL;
+    if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+    const int st = check_shape(B, H, N, d);
+    if (st != FA_OK) return st;
+    if (!good_scale(scale)) return FA_ERR_ARG;
+    if (workspace_bytes < fa_fwd_v1_workspace_bytes(B, H, N, d)) return FA_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255) != 0) return FA_ERR_WORKSPACE;
+    const size_t rows = (size_t)B * H * N;
+    char* ws = static_cast<char*>(workspace);
+    float* ows = reinterpret_cast<float*>(ws);
+    float* mws = reinterpret_cast<float*>(ws + align256(rows * d * sizeof(float)));
+    float* lws = reinterpret_cast<float*>(ws + align256(rows * d * sizeof(float)) +
+                                          align256(rows * 2 * sizeof(float)));
+    return status_of(fa::launch_fwd_v1(dtype, d, causal != 0, q, k, v, o, lse, ows, mws, lws,
+                                       B * H, N, scale, stream));
+}
+
 size_t fa_std_workspace_bytes(int B, int H, int N, int d) {
     if (check_shape(B, H, N, d) != FA_OK) return 0;
     return (size_t)B * H * N * (size_t)N * 2;  // one 16-bit N x N matrix per head

@@ -25,6 +25,9 @@ hipError_t launch_fwd_splitkv(int dtype, int d, bool causal, const void* q, cons
                               hipStream_t stream);
 hipError_t launch_lse_merge(int dtype_out, const float* o_parts, const float* lse_parts, int P,
                             long long rows, int d, void* o, float* lse, hipStream_t stream);
+hipError_t launch_fwd_v1(int dtype, int d, bool causal, const void* q, const void* k,
+                         const void* v, void* o, float* lse, float* ows, float* mws, float* lws,
+                         int BH, int N, float scale, hipStream_t stream);
 hipError_t launch_std(int dtype, int d, bool causal, const void* q, const void* k, const void* v,
                       void* o, void* s, int BH, int N, float scale, hipStream_t stream);
 

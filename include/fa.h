@@ -189,6 +189,30 @@ int fa_lse_merge(int dtype_out, int num_parts, const float* o_parts, const float
                  void* o, float* lse, int rows, int d, hipStream_t stream);
 
 /*
+ * Size in bytes of the scratch buffer fa_fwd_v1 needs: the float32 running
+ * output (B*H*N*d) and running max and sum (two copies each per row).
+ * Returns 0 for invalid shapes.
+ */
+size_t fa_fwd_v1_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * Forward pass in the first-generation loop order, for the loop-order
+ * ablation ("11.11 Flash Attention", sections "The Tiling Algorithm" and
+ * "Flash Attention 2"): one workgroup per (batch, head); the outer loop walks
+ * the K/V blocks, the inner loop the Q blocks, and for every block pair the
+ * running output O_i (float32) and statistics m_i, l_i are read from and
+ * written back to `workspace`, with O renormalised at every step. Same O and
+ * LSE as fa_fwd up to rounding; much slower (that is what it measures).
+ *   dtype, q, k, v, o, lse, B, H, N, d (64 or 128), scale, causal: as fa_fwd
+ *   (16-bit only).
+ *   workspace  at least fa_fwd_v1_workspace_bytes(B,H,N,d) bytes, 256-byte
+ *              aligned; overwritten.
+ */
+int fa_fwd_v1(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+              void* workspace, size_t workspace_bytes, int B, int H, int N, int d, float scale,
+              int causal, hipStream_t stream);
+
+/*
  * Size in bytes of the scratch buffer fa_std_fwd needs: the N x N score
  * matrix of every (batch, head) in the 16-bit input type, B*H*N*N*2 bytes
  * (S, then P written over it). Returns 0 for invalid shapes.

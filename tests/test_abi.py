@@ -216,3 +216,26 @@ def test_lse_merge_validation(lib):
     assert merge(d=6) == -2
     assert merge(d=0) == -2
     assert merge(op=ctypes.c_void_p(0x10004)) == -7  # o_parts not 16-byte aligned
+
+
+def test_v1_workspace_and_validation(lib):
+    B, H, N, d = 1, 2, 100, 64
+    rows = B * H * N
+    a256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    need = fa.fa_fwd_v1_workspace_bytes(B, H, N, d)
+    assert need == a256(rows * d * 4) + 2 * a256(rows * 2 * 4)
+    assert fa.fa_fwd_v1_workspace_bytes(B, H, N, 256) == 0
+
+    def v1(**kw):
+        a = dict(dtype=fa.FA_BF16, q=FAKE, ws=ctypes.c_void_p(0x10000), wsb=need, d=d, scale=0.1)
+        a.update(kw)
+        return lib.fa_fwd_v1(a["dtype"], a["q"], FAKE, FAKE, FAKE, None, a["ws"], a["wsb"], B, H,
+                             N, a["d"], a["scale"], 0, None)
+
+    assert v1(q=None) == -1
+    assert v1(ws=None) == -1
+    assert v1(dtype=fa.FA_F32) == -3
+    assert v1(d=256) == -4
+    assert v1(scale=0.0) == -7
+    assert v1(wsb=need - 1) == -5
+    assert v1(ws=ctypes.c_void_p(0x10040)) == -5
