@@ -13,7 +13,7 @@ Sources (web pages on FlashAttention):
   Here the statistics are saved folded into one number per row,
   LSE_i = m_i + ln(l_i), since exp(S_ij - LSE_i) = exp(S_ij - m_i) / l_i.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
 - ``scale`` multiplies Q K^T (the pages' formula uses 1/sqrt(d_k); their
   tiling pseudocode omits it). LSE is in natural-log units of the scaled
   scores.

@@ -12,7 +12,7 @@ to quantise attention inputs with a per-tensor scale amax / 448).
 
 The pages only say that FlashAttention-3 adds FP8 support ("11.11 Flash
 Attention", section "Flash Attention 3"); the choice of OCP E4M3 with a
-per-tensor scale is a reading of that, stated in the design doc.
+per-tensor scale is a reading of that (the pages name no format).
 """
 
 import numpy as np
