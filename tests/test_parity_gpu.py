@@ -339,3 +339,34 @@ def test_binding_rejects_mismatched_tensors(gpu_lib):
     with pytest.raises(gpu_lib.FAError):
         x = torch.zeros(1, 2, 64, 96, dtype=torch.bfloat16, device="cuda")
         gpu_lib.fa_fwd(x, x, x, torch.empty_like(x), None, 0.1, False)
+
+
+def test_max_size_fwd_bwd(gpu_lib):
+    """B*H*N*d just below 2^31 (the ABI's limit): every index in the kernels
+    crosses 2^30 elements. Inputs come from a seeded device generator (the
+    host would need 26 GB); the first, a middle and the last head are checked
+    against the oracle, the rest for finiteness."""
+    B, H, N, d = 511, 32, 1024, 128
+    assert B * H * N * d < 2 ** 31 and B * H * N * d > 2 ** 30 + 2 ** 29
+    note(f"max size bf16 causal B{B} H{H} N{N} d{d}")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(9001)
+    shape = (B, H, N, d)
+    q, k, v, do = (torch.randn(shape, generator=g, device="cuda", dtype=torch.float32)
+                   .to(torch.bfloat16) for _ in range(4))
+    o, lse = gpu_lib.forward(q, k, v, causal=True)
+    dq, dk, dv = gpu_lib.backward(q, k, v, o, lse, do, causal=True)
+    torch.cuda.synchronize()
+    for t in (o, lse, dq, dk, dv):
+        assert bool(torch.isfinite(t).all())
+    scale = d ** -0.5
+    for b, h in ((0, 0), (B // 2, 17), (B - 1, H - 1)):
+        args = [to64(t[b, h]) for t in (q, k, v)]
+        o_ref, l_ref = oracle.attention_forward(*args, scale, True)
+        assert max_abs(to64(o[b, h]), o_ref) <= 2e-2, (b, h)
+        assert rel_frob(to64(o[b, h]), o_ref) <= 1e-2, (b, h)
+        assert max_abs(to64(lse[b, h]), l_ref) <= 1e-3, (b, h)
+        g_ref = oracle.attention_backward(*args, to64(do[b, h]), scale, True)
+        for got, ref in zip((dq, dk, dv), g_ref):
+            assert max_abs(to64(got[b, h]), ref) <= 5e-2, (b, h)
+            assert rel_frob(to64(got[b, h]), ref) <= 1e-2, (b, h)
