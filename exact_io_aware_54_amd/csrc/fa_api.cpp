@@ -14,7 +14,7 @@ namespace {
 constexpr int kVersion = 100;  // 0.1.0
 
 // Shape checks shared by the entry points; head dims 64 and 128 everywhere,
-// 256 only where the caller allows it (the 16-bit forward).
+// 256 only where the caller allows it (the 16-bit forward and backward).
 int check_shape(int B, int H, int N, int d, bool allow256 = false) {
     if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
     if (d != 64 && d != 128 && !(allow256 && d == 256)) return FA_ERR_HEADDIM;
@@ -109,7 +109,7 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, float q_descale, 
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
-    if (check_shape(B, H, N, d) != FA_OK) return 0;
+    if (check_shape(B, H, N, d, true) != FA_OK) return 0;
     const size_t rows = (size_t)B * H * N;
     return 2 * align256(rows * sizeof(float));  // D and LSE * log2(e), one float per row each
 }
@@ -121,7 +121,7 @@ int bwd_common(int dtype, const void* q, const void* k, const void* v, const voi
                int stages, hipStream_t stream) {
     if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
     if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
-    const int st = check_shape(B, H, N, d);
+    const int st = check_shape(B, H, N, d, true);
     if (st != FA_OK) return st;
     if (!good_scale(scale)) return FA_ERR_ARG;
     if (workspace_bytes < fa_bwd_workspace_bytes(B, H, N, d)) return FA_ERR_WORKSPACE;

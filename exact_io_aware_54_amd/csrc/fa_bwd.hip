@@ -353,6 +353,207 @@ bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     }
 }
 
+// ---------------------------------------------------------------- 2b. dK or dV, d = 256
+// At head dim 256 the eight-wave pass does not fit: its dK and dV
+// accumulators alone would take every register of a wave. Here four waves,
+// one per SIMD, each own 32 keys of a 128-key block with their K (and V) rows
+// in registers and walk the query blocks 32 rows at a time; one launch
+// accumulates dV = P^T dO, a second one dK = scale dS^T Q (recomputing S and
+// computing dP), so a wave holds one accumulator of 32 keys x 256 dims.
+template <int D>
+struct Dkdv1Tile {
+    static constexpr int BN = 128;               // keys per workgroup (4 waves x 32)
+    static constexpr int BM = 32;                // queries per step
+    static constexpr int NT = 256;
+    static constexpr int ROWB = 2 * D;
+    static constexpr int QTILEB = BM * ROWB;     // bytes of one Q (or dO) tile
+    static constexpr int NLOADQ = QTILEB / (NT * 16);
+    static constexpr int KS = D / 16;
+    static constexpr int DB = D / 32;
+    static_assert(NLOADQ >= 1 && QTILEB % (NT * 16) == 0, "tile must split into whole loads");
+};
+
+template <typename T, int D, bool CAUSAL, bool DK>
+struct Dkdv1Wave {
+    using C = Dkdv1Tile<D>;
+    using V8 = typename Vec<T>::x8;
+    using V4 = typename Vec<T>::x4;
+
+    const T* Qh;
+    const T* dOh;
+    const float* lse2h;
+    const float* delh;
+    int N, tid, lane, wave, l32, h, key0, key;
+    float c;
+    V8 kf[C::KS], vf[DK ? C::KS : 1];   // B operands: K (and V) rows of this lane's key
+    int ld_row[C::NLOADQ], ld_col[C::NLOADQ];
+    f32x16 acc[C::DB];                  // dK^T or dV^T: head dim in registers, key = lane
+
+    __device__ __forceinline__ void init(const T* Qh_, const T* Kh, const T* Vh, const T* dOh_,
+                                         const float* lse2h_, const float* delh_, int N_, int kb,
+                                         float c_) {
+        Qh = Qh_;
+        dOh = dOh_;
+        lse2h = lse2h_;
+        delh = delh_;
+        N = N_;
+        c = c_;
+        tid = threadIdx.x;
+        lane = tid & 63;
+        wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        l32 = lane & 31;
+        h = lane >> 5;
+        key0 = kb * C::BN + 32 * wave;
+        key = key0 + l32;
+        const int kr = min(key, N - 1);
+        const V8* ks = reinterpret_cast<const V8*>(Kh + (size_t)kr * D + 8 * h);
+#pragma unroll
+        for (int s = 0; s < C::KS; ++s) kf[s] = ks[2 * s];
+        if (DK) {
+            const V8* vs = reinterpret_cast<const V8*>(Vh + (size_t)kr * D + 8 * h);
+#pragma unroll
+            for (int s = 0; s < C::KS; ++s) vf[s] = vs[2 * s];
+        }
+#pragma unroll
+        for (int i = 0; i < C::NLOADQ; ++i) {
+            const int byte = i * (C::NT * 16) + tid * 16;
+            const int r = byte / C::ROWB, p = (byte % C::ROWB) / 16;
+            ld_row[i] = r;
+            ld_col[i] = (p ^ tile_swz<D>(r)) * 8;
+        }
+#pragma unroll
+        for (int b = 0; b < C::DB; ++b) acc[b] = f32x16{};
+    }
+
+    // Q and dO rows [qbase, qbase + BM) and their LSE2 / D into one buffer set
+    // (the 4-byte loads fill 64 entries; rows past the block read clamped rows).
+    __device__ __forceinline__ void issue(int qbase, char* sQd, char* sGd, float* sLd,
+                                          float* sDd) const {
+#pragma unroll
+        for (int i = 0; i < C::NLOADQ; ++i) {
+            const size_t row = (size_t)min(qbase + ld_row[i], N - 1) * D;
+            const int o = i * (C::NT * 16) + wave * 1024;
+            __builtin_amdgcn_global_load_lds(Qh + row + ld_col[i], sQd + o, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(dOh + row + ld_col[i], sGd + o, 16, 0, 0);
+        }
+        const int r = min(qbase + lane, N - 1);
+        if (wave == 0) __builtin_amdgcn_global_load_lds(lse2h + r, sLd, 4, 0, 0);
+        if (DK && wave == 1) __builtin_amdgcn_global_load_lds(delh + r, sDd, 4, 0, 0);
+    }
+
+    __device__ __forceinline__ void step(int ib, int nqb, const char* sQ, const char* sG,
+                                         const float* sL, const float* sD, char* nQ, char* nG,
+                                         float* nL, float* nD) {
+        const int qbase = ib * C::BM;
+        __builtin_amdgcn_s_waitcnt(kVmcntZero);
+        __syncthreads();
+        if (ib + 1 < nqb) issue(qbase + C::BM, nQ, nG, nL, nD);
+        if (CAUSAL && key0 > qbase + C::BM - 1) return;  // every query of the block precedes every key
+
+        // S = Q K^T (and dP = dO V^T): lane = key, register r = query qbase + acc_row(r, h)
+        f32x16 sacc = f32x16{}, pacc = f32x16{};
+#pragma unroll
+        for (int s = 0; s < C::KS; ++s) {
+            const int ro = tile_off<D>(l32, 16 * s + 8 * h);
+            const V8 aq = *reinterpret_cast<const V8*>(sQ + ro);
+            sacc = mfma32(aq, kf[s], sacc);
+            if (DK) {
+                const V8 ag = *reinterpret_cast<const V8*>(sG + ro);
+                pacc = mfma32(ag, vf[DK ? s : 0], pacc);
+            }
+        }
+        const bool need_mask = key0 + 31 >= N || qbase + 31 >= N || (CAUSAL && key0 + 31 > qbase);
+        const int lo = key - qbase - 4 * h;   // causal-visible iff const(r) >= lo
+        const int hi = N - qbase - 4 * h;     // query < N iff const(r) < hi
+        const bool kvalid = key < N;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 lq = *reinterpret_cast<const f32x4*>(sL + 8 * r4 + 4 * h);
+            const f32x4 dq = DK ? *reinterpret_cast<const f32x4*>(sD + 8 * r4 + 4 * h)
+                                : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * r4 + i;
+                float l2 = lq[i];
+                if (need_mask) {
+                    const int cr = 8 * r4 + i;
+                    const bool vis = kvalid && cr < hi && (!CAUSAL || cr >= lo);
+                    if (!vis) l2 = INFINITY;
+                }
+                const float p = fast_exp2(fmaf(sacc[r], c, -l2));
+                if (DK) pacc[r] = p * (pacc[r] - dq[i]);
+                else sacc[r] = p;
+            }
+        }
+        V8 op[2];
+        op[0] = pack8<T>(DK ? pacc : sacc, 0);
+        op[1] = pack8<T>(DK ? pacc : sacc, 8);
+        // dV^T += dO^T P or dK^T += Q^T dS, dO^T / Q^T read transposed: this lane
+        // supplies row 16 g2 + 8 half + 4 h + (lane % 16) / 4, head dims 32 b +
+        // 16 ((lane / 16) % 2) + 4 (lane % 4); it receives head dim 32 b + lane %
+        // 32 at queries 16 g2 + 8 half + 4 h + 0..3 (registers 8 g2 + 4 half + 0..3)
+        const char* src = DK ? sQ : sG;
+        const int src_r = 4 * h + (lane & 15) / 4;
+        const int src_d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+        for (int g2 = 0; g2 < 2; ++g2)
+#pragma unroll
+            for (int b = 0; b < C::DB; ++b) {
+                const V8 a = tr_read8<V8>(src, tile_off<D>(16 * g2 + src_r, 32 * b + src_d),
+                                          tile_off<D>(16 * g2 + 8 + src_r, 32 * b + src_d));
+                acc[b] = mfma32(a, op[g2], acc[b]);
+            }
+    }
+
+    __device__ __forceinline__ void finish(T* outh, float mul) const {
+        if (key >= N) return;
+        T* row = outh + (size_t)key * D;
+#pragma unroll
+        for (int b = 0; b < C::DB; ++b)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                V4 w;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w[i] = (T)(acc[b][4 * r4 + i] * mul);
+                *reinterpret_cast<V4*>(row + 32 * b + 8 * r4 + 4 * h) = w;
+            }
+    }
+};
+
+template <typename T, int D, bool CAUSAL, bool DK>
+__global__ void __launch_bounds__(256, 1)
+bwd_dkdv1_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+                 const T* __restrict__ dO, const float* __restrict__ lse2,
+                 const float* __restrict__ delta, T* __restrict__ out, int BH, int N, int nkb,
+                 float scale, float c) {
+    using C = Dkdv1Tile<D>;
+    __shared__ __attribute__((aligned(1024))) char sQ0[C::QTILEB];
+    __shared__ __attribute__((aligned(1024))) char sQ1[C::QTILEB];
+    __shared__ __attribute__((aligned(1024))) char sG0[C::QTILEB];
+    __shared__ __attribute__((aligned(1024))) char sG1[C::QTILEB];
+    __shared__ __attribute__((aligned(256))) float sL0[64];
+    __shared__ __attribute__((aligned(256))) float sL1[64];
+    __shared__ __attribute__((aligned(256))) float sD0[64];
+    __shared__ __attribute__((aligned(256))) float sD1[64];
+
+    const int L = xcd_remap(blockIdx.x, BH * nkb);
+    const int bh = L / nkb;
+    const int kb = L % nkb;
+    const size_t head = (size_t)bh * N * D;
+    const size_t rowbase = (size_t)bh * N;
+
+    Dkdv1Wave<T, D, CAUSAL, DK> w;
+    w.init(Q + head, K + head, V + head, dO + head, lse2 + rowbase, delta + rowbase, N, kb, c);
+    const int nqb = (N + C::BM - 1) / C::BM;
+    const int i0 = CAUSAL ? (kb * C::BN) / C::BM : 0;
+    w.issue(i0 * C::BM, sQ0, sG0, sL0, sD0);
+    for (int ib = i0; ib < nqb; ib += 2) {
+        w.step(ib, nqb, sQ0, sG0, sL0, sD0, sQ1, sG1, sL1, sD1);
+        if (ib + 1 < nqb) w.step(ib + 1, nqb, sQ1, sG1, sL1, sD1, sQ0, sG0, sL0, sD0);
+    }
+    w.finish(out + head, DK ? scale : 1.f);
+}
+
 // ---------------------------------------------------------------- 3. dQ
 template <int D>
 struct DqTile {
@@ -515,7 +716,7 @@ struct DqWave {
 };
 
 template <typename T, int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(256, D > 128 ? 1 : 2)
 bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
               const T* __restrict__ dO, const float* __restrict__ lse2,
               const float* __restrict__ delta, T* __restrict__ dQ, int BH, int N, int nqb,
@@ -561,10 +762,21 @@ hipError_t launch_typed(const void* q, const void* k, const void* v, const void*
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (stages & 2) {
-        const int nkb = (N + DkdvTile<D>::BN - 1) / DkdvTile<D>::BN;
-        hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3(BH * nkb), dim3(DkdvTile<D>::NT), 0, stream,
-                           tq, tk, tv, tdo, lse2, delta, static_cast<T*>(dk), static_cast<T*>(dv),
-                           BH, N, nkb, scale, c);
+        if constexpr (D > 128) {
+            const int nkb = (N + Dkdv1Tile<D>::BN - 1) / Dkdv1Tile<D>::BN;
+            hipLaunchKernelGGL((bwd_dkdv1_kernel<T, D, CAUSAL, false>), dim3(BH * nkb), dim3(256),
+                               0, stream, tq, tk, tv, tdo, lse2, delta, static_cast<T*>(dv), BH,
+                               N, nkb, scale, c);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            hipLaunchKernelGGL((bwd_dkdv1_kernel<T, D, CAUSAL, true>), dim3(BH * nkb), dim3(256),
+                               0, stream, tq, tk, tv, tdo, lse2, delta, static_cast<T*>(dk), BH,
+                               N, nkb, scale, c);
+        } else {
+            const int nkb = (N + DkdvTile<D>::BN - 1) / DkdvTile<D>::BN;
+            hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3(BH * nkb),
+                               dim3(DkdvTile<D>::NT), 0, stream, tq, tk, tv, tdo, lse2, delta,
+                               static_cast<T*>(dk), static_cast<T*>(dv), BH, N, nkb, scale, c);
+        }
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (stages & 4) {
@@ -587,6 +799,11 @@ hipError_t launch_d(int d, bool causal, const void* q, const void* k, const void
                                                   BH, N, scale, stages, stream)
                       : launch_typed<T, 64, false>(q, k, v, o, lse, dO, dq, dk, dv, delta, lse2,
                                                    BH, N, scale, stages, stream);
+    if (d == 256)
+        return causal ? launch_typed<T, 256, true>(q, k, v, o, lse, dO, dq, dk, dv, delta, lse2,
+                                                   BH, N, scale, stages, stream)
+                      : launch_typed<T, 256, false>(q, k, v, o, lse, dO, dq, dk, dv, delta,
+                                                    lse2, BH, N, scale, stages, stream);
     return causal ? launch_typed<T, 128, true>(q, k, v, o, lse, dO, dq, dk, dv, delta, lse2, BH,
                                                N, scale, stages, stream)
                   : launch_typed<T, 128, false>(q, k, v, o, lse, dO, dq, dk, dv, delta, lse2, BH,

@@ -24,8 +24,8 @@
  *    caller. The library allocates no memory and keeps no per-call state.
  *  - Layout: contiguous row-major [B, H, N, d] for Q, K, V, O, dO, dQ, dK, dV;
  *    LSE is [B, H, N] float32 (natural log, of the scaled scores).
- *  - d must be 64 or 128 (the 16-bit fa_fwd also takes 256). B, H, N >= 1
- *    and B*H*N*d < 2^31.
+ *  - d must be 64 or 128 (the 16-bit fa_fwd and fa_bwd also take 256).
+ *    B, H, N >= 1 and B*H*N*d < 2^31.
  *  - causal != 0: query i attends to keys 0..i (the mask is not on the pages;
  *    it is the usual lower-triangular mask with N_q = N_k).
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
@@ -114,8 +114,10 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
  *   dq, dk, dv [B,H,N,d] of `dtype`, written.
  *   workspace  device scratch of at least fa_bwd_workspace_bytes(B,H,N,d)
  *              bytes, 256-byte aligned; overwritten (no initial value needed).
+ *   d          64, 128 or 256.
  * dK/dV and dQ are produced by two separate passes over the score tiles (no
- * atomics), so all three outputs are bitwise deterministic.
+ * atomics), so all three outputs are bitwise deterministic. At d = 256 the
+ * dK/dV pass is two launches (dV, then dK), each recomputing the scores.
  */
 int fa_bwd(int dtype, const void* q, const void* k, const void* v, const void* o,
            const float* lse, const void* dO, void* dq, void* dk, void* dv,

@@ -113,7 +113,7 @@ def test_bwd_validation(lib):
     assert bwd(ws=None) == -1
     assert bwd(dtype=fa.FA_F32) == -3
     assert bwd(d=80) == -4
-    assert bwd(d=256) == -4
+    assert bwd(d=512) == -4
     assert bwd(wsb=need - 1) == -5
     assert bwd(ws=ctypes.c_void_p(0x10010)) == -5  # not 256-byte aligned
     assert bwd(scale=0.0) == -7

@@ -199,6 +199,36 @@ def test_bwd_16bit_small(gpu_lib, dtype, d, causal, N):
         assert rel_frob(g, r) <= 1e-2, name
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 17, 64, 130, 300])
+def test_bwd_d256_small(gpu_lib, dtype, causal, N):
+    d = 256
+    (dq, dk, dv), ref = check_bwd_full(gpu_lib, dtype, 1, 2, N, d, causal, 8500 + N)
+    for got, exp in zip((dq, dk, dv), ref):
+        assert max_abs(got, exp) <= 5e-2
+        assert rel_frob(got, exp) <= 1e-2
+
+
+def test_bwd_d256_workload(gpu_lib):
+    """Head dim 256 backward at a training-like shape, every element of two heads."""
+    B, H, N, d = 2, 8, 2048, 256
+    note(f"bwd bf16 causal B{B} H{H} N{N} d{d}")
+    q, k, v, do = inputs.draw_qkv(B, H, N, d, 8601, torch.bfloat16, with_do=True)
+    qg, kg, vg, dog = dev(q, k, v, do)
+    o, lse = gpu_lib.forward(qg, kg, vg, causal=True)
+    dq, dk, dv = gpu_lib.backward(qg, kg, vg, o, lse, dog, causal=True)
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv):
+        assert bool(torch.isfinite(t).all())
+    for b, h in ((0, 0), (1, 7)):
+        ref = oracle.attention_backward(to64(q[b, h]), to64(k[b, h]), to64(v[b, h]),
+                                        to64(do[b, h]), d ** -0.5, True)
+        for got, exp in zip((dq, dk, dv), ref):
+            assert max_abs(to64(got[b, h]), exp) <= 5e-2, (b, h)
+            assert rel_frob(to64(got[b, h]), exp) <= 1e-2, (b, h)
+
+
 def test_fwd_bwd_training_workload(gpu_lib):
     """B8 H16 N4096 d128 causal bf16: the shape the benchmark times."""
     B, H, N, d = 8, 16, 4096, 128
