@@ -9,11 +9,12 @@ in the library's kernels; there is no fallback path. If the library has not
 been built, calls raise ``RuntimeError``.
 
 Entry points: ``fa_fwd``, ``fa_fwd_fp8``, ``fa_bwd``, ``fa_bwd_stage``,
-``fa_bwd_workspace_bytes``, ``fa_fwd_splitkv``,
+``fa_bwd_workspace_bytes``, ``fa_bwd_fp8``, ``fa_bwd_fp8_workspace_bytes``,
+``fa_fwd_splitkv``,
 ``fa_fwd_splitkv_workspace_bytes``, ``fa_lse_merge``, ``fa_fwd_v1``,
 ``fa_fwd_v1_workspace_bytes``, ``fa_std_fwd``,
 ``fa_std_workspace_bytes``, ``fa_status_string``, ``fa_version``;
-``forward`` / ``backward`` / ``forward_fp8`` / ``forward_splitkv`` /
+``forward`` / ``backward`` / ``forward_fp8`` / ``backward_fp8`` / ``forward_splitkv`` /
 ``forward_v1`` / ``forward_standard`` allocate outputs with torch and call them.
 """
 
@@ -66,6 +67,11 @@ def load_library(path=None):
     lib.fa_fwd_splitkv.restype = i
     lib.fa_lse_merge.argtypes = [i, i, vp, vp, vp, vp, i, i, vp]
     lib.fa_lse_merge.restype = i
+    lib.fa_bwd_fp8_workspace_bytes.argtypes = [i, i, i, i]
+    lib.fa_bwd_fp8_workspace_bytes.restype = sz
+    lib.fa_bwd_fp8.argtypes = [vp, vp, vp, f, f, f, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f,
+                               i, vp]
+    lib.fa_bwd_fp8.restype = i
     lib.fa_fwd_v1_workspace_bytes.argtypes = [i, i, i, i]
     lib.fa_fwd_v1_workspace_bytes.restype = sz
     lib.fa_fwd_v1.argtypes = [i, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, vp]
@@ -243,6 +249,30 @@ def fa_lse_merge(o_parts, lse_parts, o, lse=None, stream=None):
     _raise("fa_lse_merge", st)
 
 
+def fa_bwd_fp8_workspace_bytes(B, H, N, d):
+    return int(load_library().fa_bwd_fp8_workspace_bytes(B, H, N, d))
+
+
+def fa_bwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, o, lse, do, dq, dk, dv, workspace,
+               scale, causal, stream=None):
+    """Gradients w.r.t. the dequantised fp8 inputs; o, do, dq, dk, dv are bfloat16."""
+    import torch
+    lib = load_library()
+    B, H, N, d = q8.shape
+    for name, t in (("q8", q8), ("k8", k8), ("v8", v8)):
+        _check_bhnd(name, t, (B, H, N, d), torch.uint8)
+    for name, t in (("o", o), ("do", do), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_bhnd(name, t, (B, H, N, d), torch.bfloat16)
+    _check_bhnd("lse", lse, (B, H, N), torch.float32)
+    if workspace.dtype != torch.uint8 or not workspace.is_cuda:
+        raise TypeError("workspace must be a uint8 device tensor")
+    st = lib.fa_bwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), float(q_descale), float(k_descale),
+                        float(v_descale), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
+                        _ptr(dv), _ptr(workspace), workspace.numel(), B, H, N, d, float(scale),
+                        int(bool(causal)), _stream(stream))
+    _raise("fa_bwd_fp8", st)
+
+
 def fa_fwd_v1_workspace_bytes(B, H, N, d):
     return int(load_library().fa_fwd_v1_workspace_bytes(B, H, N, d))
 
@@ -307,6 +337,19 @@ def forward_splitkv(q, k, v, scale=None, causal=False, num_splits=0):
                      device=q.device, dtype=torch.uint8)
     fa_fwd_splitkv(q, k, v, o, lse, ws, scale, causal, num_splits)
     return o, lse
+
+
+def backward_fp8(q8, k8, v8, descales, o, lse, do, scale=None, causal=False):
+    """Allocate dQ, dK, dV (bfloat16) and the workspace with torch and run fa_bwd_fp8."""
+    import torch
+    B, H, N, d = q8.shape
+    scale = d ** -0.5 if scale is None else scale
+    dq, dk, dv = (torch.empty((B, H, N, d), device=q8.device, dtype=torch.bfloat16)
+                  for _ in range(3))
+    ws = torch.empty(fa_bwd_fp8_workspace_bytes(B, H, N, d), device=q8.device, dtype=torch.uint8)
+    fa_bwd_fp8(q8, k8, v8, descales[0], descales[1], descales[2], o, lse, do, dq, dk, dv, ws,
+               scale, causal)
+    return dq, dk, dv
 
 
 def forward_v1(q, k, v, scale=None, causal=False):

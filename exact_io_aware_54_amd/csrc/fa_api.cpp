@@ -29,6 +29,14 @@ int status_of(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// The kernels move tensors in 16-byte vectors: every [.., N, d] tensor must
+// start on a 16-byte boundary, float32 row statistics on a 4-byte one.
+template <typename... P>
+bool aligned16(const P*... p) {
+    return ((((uintptr_t)p & 15) == 0) && ...);
+}
+bool aligned4(const float* p) { return ((uintptr_t)p & 3) == 0; }
+
 // Key ranges of fa_fwd_splitkv: whole 128-key tiles, as evenly as possible.
 // num_splits = 0 picks enough ranges for about two workgroups per CU.
 struct SplitPlan {
@@ -82,6 +90,7 @@ int fa_fwd(int dtype, const void* q, const void* k, const void* v, void* o, floa
     const int st = check_shape(B, H, N, d, dtype != FA_F32);
     if (st != FA_OK) return st;
     if (!good_scale(scale)) return FA_ERR_ARG;
+    if (!aligned16(q, k, v, o) || !aligned4(lse)) return FA_ERR_ARG;
     const int BH = B * H;
     if (dtype == FA_F32)
         return status_of(fa::launch_fwd_f32(d, causal != 0, static_cast<const float*>(q),
@@ -104,6 +113,7 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, float q_descale, 
         return FA_ERR_ARG;
     const float qk = scale * q_descale * k_descale;
     if (!good_scale(qk)) return FA_ERR_ARG;
+    if (!aligned16(q8, k8, v8, o_bf16) || !aligned4(lse)) return FA_ERR_ARG;
     return status_of(fa::launch_fwd_fp8(d, causal != 0, q8, k8, v8, qk, v_descale, o_bf16, lse,
                                         B * H, N, stream));
 }
@@ -124,6 +134,7 @@ int bwd_common(int dtype, const void* q, const void* k, const void* v, const voi
     const int st = check_shape(B, H, N, d, true);
     if (st != FA_OK) return st;
     if (!good_scale(scale)) return FA_ERR_ARG;
+    if (!aligned16(q, k, v, o, dO, dq, dk, dv) || !aligned4(lse)) return FA_ERR_ARG;
     if (workspace_bytes < fa_bwd_workspace_bytes(B, H, N, d)) return FA_ERR_WORKSPACE;
     if (((uintptr_t)workspace & 255) != 0) return FA_ERR_WORKSPACE;
     const size_t rows = (size_t)B * H * N;
@@ -152,6 +163,48 @@ int fa_bwd_stage(int stage, int dtype, const void* q, const void* k, const void*
                       d, scale, causal, 1 << (stage - 1), stream);
 }
 
+size_t fa_bwd_fp8_workspace_bytes(int B, int H, int N, int d) {
+    if (check_shape(B, H, N, d, true) != FA_OK) return 0;
+    const size_t el = (size_t)B * H * N * d;
+    return 3 * align256(el * 2) + fa_bwd_workspace_bytes(B, H, N, d);
+}
+
+int fa_bwd_fp8(const void* q8, const void* k8, const void* v8, float q_descale, float k_descale,
+               float v_descale, const void* o_bf16, const float* lse, const void* dO_bf16,
+               void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B,
+               int H, int N, int d, float scale, int causal, hipStream_t stream) {
+    if (!q8 || !k8 || !v8 || !o_bf16 || !lse || !dO_bf16 || !dq || !dk || !dv || !workspace)
+        return FA_ERR_NULL;
+    const int st = check_shape(B, H, N, d, true);
+    if (st != FA_OK) return st;
+    if (!good_scale(scale) || !good_scale(q_descale) || !good_scale(k_descale) ||
+        !good_scale(v_descale))
+        return FA_ERR_ARG;
+    const float c = scale * q_descale * k_descale * 1.4426950408889634f;
+    const float dk_mul = scale * q_descale * v_descale, dq_mul = scale * k_descale * v_descale;
+    const float d_mul = 1.f / v_descale;
+    if (!good_scale(c) || !good_scale(dk_mul) || !good_scale(dq_mul) || !good_scale(d_mul))
+        return FA_ERR_ARG;
+    if (!aligned16(q8, k8, v8, o_bf16, dO_bf16, dq, dk, dv) || !aligned4(lse)) return FA_ERR_ARG;
+    if (workspace_bytes < fa_bwd_fp8_workspace_bytes(B, H, N, d)) return FA_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255) != 0) return FA_ERR_WORKSPACE;
+    const size_t el = (size_t)B * H * N * d, rows = (size_t)B * H * N;
+    char* ws = static_cast<char*>(workspace);
+    void* qc = ws;
+    void* kc = ws + align256(el * 2);
+    void* vc = ws + 2 * align256(el * 2);
+    float* delta = reinterpret_cast<float*>(ws + 3 * align256(el * 2));
+    float* lse2 = reinterpret_cast<float*>(ws + 3 * align256(el * 2) + align256(rows * 4));
+    hipError_t e;
+    if ((e = fa::launch_e4m3_to_bf16(q8, qc, el, stream)) != hipSuccess) return FA_ERR_HIP;
+    if ((e = fa::launch_e4m3_to_bf16(k8, kc, el, stream)) != hipSuccess) return FA_ERR_HIP;
+    if ((e = fa::launch_e4m3_to_bf16(v8, vc, el, stream)) != hipSuccess) return FA_ERR_HIP;
+    const fa::BwdScales sc{c, dk_mul, dq_mul, d_mul};
+    return status_of(fa::launch_bwd_scaled(FA_BF16, d, causal != 0, qc, kc, vc, o_bf16, lse,
+                                           dO_bf16, dq, dk, dv, delta, lse2, B * H, N, sc, 7,
+                                           stream));
+}
+
 size_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits) {
     if (splitkv_shape(B, H, Nq, Nk, d, num_splits) != FA_OK) return 0;
     const SplitPlan pl = splitkv_plan(B, H, Nq, Nk, num_splits);
@@ -168,6 +221,7 @@ int fa_fwd_splitkv(int dtype, const void* q, const void* k, const void* v, void*
     if (st != FA_OK) return st;
     if (causal && Nq > Nk) return FA_ERR_SHAPE;
     if (!good_scale(scale)) return FA_ERR_ARG;
+    if (!aligned16(q, k, v, o) || !aligned4(lse)) return FA_ERR_ARG;
     if (workspace_bytes < fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, num_splits))
         return FA_ERR_WORKSPACE;
     if (((uintptr_t)workspace & 255) != 0) return FA_ERR_WORKSPACE;
@@ -189,7 +243,8 @@ int fa_lse_merge(int dtype_out, int num_parts, const float* o_parts, const float
     if (dtype_out != FA_F32 && dtype_out != FA_F16 && dtype_out != FA_BF16) return FA_ERR_DTYPE;
     if (num_parts < 1 || rows < 1 || d < 4 || d % 4 != 0 || d > 65536) return FA_ERR_SHAPE;
     if ((int64_t)rows * (d / 4) >= ((int64_t)1 << 38)) return FA_ERR_SHAPE;
-    if (((uintptr_t)o_parts & 15) != 0) return FA_ERR_ARG;
+    if (!aligned16(o_parts) || !aligned4(lse_parts) || !aligned4(lse)) return FA_ERR_ARG;
+    if (((uintptr_t)o & (dtype_out == FA_F32 ? 3 : 1)) != 0) return FA_ERR_ARG;
     return status_of(fa::launch_lse_merge(dtype_out, o_parts, lse_parts, num_parts, rows, d, o, lse,
                                           stream));
 }
@@ -208,6 +263,7 @@ int fa_fwd_v1(int dtype, const void* q, const void* k, const void* v, void* o, f
     const int st = check_shape(B, H, N, d);
     if (st != FA_OK) return st;
     if (!good_scale(scale)) return FA_ERR_ARG;
+    if (!aligned16(q, k, v, o) || !aligned4(lse)) return FA_ERR_ARG;
     if (workspace_bytes < fa_fwd_v1_workspace_bytes(B, H, N, d)) return FA_ERR_WORKSPACE;
     if (((uintptr_t)workspace & 255) != 0) return FA_ERR_WORKSPACE;
     const size_t rows = (size_t)B * H * N;
@@ -234,6 +290,7 @@ int fa_std_fwd(int dtype, const void* q, const void* k, const void* v, void* o, 
     if (st != FA_OK) return st;
     if ((int64_t)B * H > 65535) return FA_ERR_SHAPE;
     if (!good_scale(scale)) return FA_ERR_ARG;
+    if (!aligned16(q, k, v, o)) return FA_ERR_ARG;
     if (workspace_bytes < fa_std_workspace_bytes(B, H, N, d)) return FA_ERR_WORKSPACE;
     if (((uintptr_t)workspace & 255) != 0) return FA_ERR_WORKSPACE;
     return status_of(

@@ -55,7 +55,7 @@ __device__ __forceinline__ V8 tr_read8(const char* base, int off_lo, int off_hi)
 template <typename T, int D>
 __global__ void __launch_bounds__(256)
 bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO, const float* __restrict__ lse,
-               float* __restrict__ delta, float* __restrict__ lse2, int rows) {
+               float* __restrict__ delta, float* __restrict__ lse2, int rows, float d_mul) {
     using V8 = typename Vec<T>::x8;
     constexpr int TPR = D / 8;  // threads per row
     const int gid = blockIdx.x * 256 + threadIdx.x;
@@ -70,7 +70,7 @@ bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO, const float* _
 #pragma unroll
     for (int off = TPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, TPR);
     if (row < rows && part == 0) {
-        delta[row] = s;
+        delta[row] = s * d_mul;
         lse2[row] = lse[row] * kLog2e;
     }
 }
@@ -746,10 +746,10 @@ bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
 template <typename T, int D, bool CAUSAL>
 hipError_t launch_typed(const void* q, const void* k, const void* v, const void* o,
                         const float* lse, const void* dO, void* dq, void* dk, void* dv,
-                        float* delta, float* lse2, int BH, int N, float scale, int stages,
+                        float* delta, float* lse2, int BH, int N, const BwdScales& sc, int stages,
                         hipStream_t stream) {
     const int rows = BH * N;
-    const float c = scale * kLog2e;
+    const float c = sc.c;
     auto tq = static_cast<const T*>(q);
     auto tk = static_cast<const T*>(k);
     auto tv = static_cast<const T*>(v);
@@ -758,7 +758,7 @@ hipError_t launch_typed(const void* q, const void* k, const void* v, const void*
     if (stages & 1) {
         const int threads = rows * (D / 8);
         hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((threads + 255) / 256), dim3(256), 0,
-                           stream, static_cast<const T*>(o), tdo, lse, delta, lse2, rows);
+                           stream, static_cast<const T*>(o), tdo, lse, delta, lse2, rows, sc.d_mul);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (stages & 2) {
@@ -766,24 +766,25 @@ hipError_t launch_typed(const void* q, const void* k, const void* v, const void*
             const int nkb = (N + Dkdv1Tile<D>::BN - 1) / Dkdv1Tile<D>::BN;
             hipLaunchKernelGGL((bwd_dkdv1_kernel<T, D, CAUSAL, false>), dim3(BH * nkb), dim3(256),
                                0, stream, tq, tk, tv, tdo, lse2, delta, static_cast<T*>(dv), BH,
-                               N, nkb, scale, c);
+                               N, nkb, sc.dk_mul, c);
             if ((e = hipGetLastError()) != hipSuccess) return e;
             hipLaunchKernelGGL((bwd_dkdv1_kernel<T, D, CAUSAL, true>), dim3(BH * nkb), dim3(256),
                                0, stream, tq, tk, tv, tdo, lse2, delta, static_cast<T*>(dk), BH,
-                               N, nkb, scale, c);
+                               N, nkb, sc.dk_mul, c);
         } else {
             const int nkb = (N + DkdvTile<D>::BN - 1) / DkdvTile<D>::BN;
             hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3(BH * nkb),
                                dim3(DkdvTile<D>::NT), 0, stream, tq, tk, tv, tdo, lse2, delta,
-                               static_cast<T*>(dk), static_cast<T*>(dv), BH, N, nkb, scale, c);
+                               static_cast<T*>(dk), static_cast<T*>(dv), BH, N, nkb, sc.dk_mul,
+                               c);
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (stages & 4) {
         const int nqb = (N + DqTile<D>::BM - 1) / DqTile<D>::BM;
         hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3(BH * nqb), dim3(256), 0, stream,
-                           tq, tk, tv, tdo, lse2, delta, static_cast<T*>(dq), BH, N, nqb, scale,
-                           c);
+                           tq, tk, tv, tdo, lse2, delta, static_cast<T*>(dq), BH, N, nqb,
+                           sc.dq_mul, c);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return e;
@@ -792,35 +793,44 @@ hipError_t launch_typed(const void* q, const void* k, const void* v, const void*
 template <typename T>
 hipError_t launch_d(int d, bool causal, const void* q, const void* k, const void* v,
                     const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv,
-                    float* delta, float* lse2, int BH, int N, float scale, int stages,
+                    float* delta, float* lse2, int BH, int N, const BwdScales& sc, int stages,
                     hipStream_t stream) {
     if (d == 64)
         return causal ? launch_typed<T, 64, true>(q, k, v, o, lse, dO, dq, dk, dv, delta, lse2,
-                                                  BH, N, scale, stages, stream)
+                                                  BH, N, sc, stages, stream)
                       : launch_typed<T, 64, false>(q, k, v, o, lse, dO, dq, dk, dv, delta, lse2,
-                                                   BH, N, scale, stages, stream);
+                                                   BH, N, sc, stages, stream);
     if (d == 256)
         return causal ? launch_typed<T, 256, true>(q, k, v, o, lse, dO, dq, dk, dv, delta, lse2,
-                                                   BH, N, scale, stages, stream)
+                                                   BH, N, sc, stages, stream)
                       : launch_typed<T, 256, false>(q, k, v, o, lse, dO, dq, dk, dv, delta,
-                                                    lse2, BH, N, scale, stages, stream);
+                                                    lse2, BH, N, sc, stages, stream);
     return causal ? launch_typed<T, 128, true>(q, k, v, o, lse, dO, dq, dk, dv, delta, lse2, BH,
-                                               N, scale, stages, stream)
+                                               N, sc, stages, stream)
                   : launch_typed<T, 128, false>(q, k, v, o, lse, dO, dq, dk, dv, delta, lse2, BH,
-                                                N, scale, stages, stream);
+                                                N, sc, stages, stream);
 }
 
 }  // namespace
+
+hipError_t launch_bwd_scaled(int dtype, int d, bool causal, const void* q, const void* k,
+                             const void* v, const void* o, const float* lse, const void* dO,
+                             void* dq, void* dk, void* dv, float* delta, float* lse2, int BH,
+                             int N, const BwdScales& sc, int stages, hipStream_t stream) {
+    if (dtype == 2)
+        return launch_d<__bf16>(d, causal, q, k, v, o, lse, dO, dq, dk, dv, delta, lse2, BH, N,
+                                sc, stages, stream);
+    return launch_d<_Float16>(d, causal, q, k, v, o, lse, dO, dq, dk, dv, delta, lse2, BH, N,
+                              sc, stages, stream);
+}
 
 hipError_t launch_bwd(int dtype, int d, bool causal, const void* q, const void* k, const void* v,
                       const void* o, const float* lse, const void* dO, void* dq, void* dk,
                       void* dv, float* delta, float* lse2, int BH, int N, float scale,
                       int stages, hipStream_t stream) {
-    if (dtype == 2)
-        return launch_d<__bf16>(d, causal, q, k, v, o, lse, dO, dq, dk, dv, delta, lse2, BH, N,
-                                scale, stages, stream);
-    return launch_d<_Float16>(d, causal, q, k, v, o, lse, dO, dq, dk, dv, delta, lse2, BH, N,
-                              scale, stages, stream);
+    const BwdScales sc{scale * kLog2e, scale, scale, 1.f};
+    return launch_bwd_scaled(dtype, d, causal, q, k, v, o, lse, dO, dq, dk, dv, delta, lse2, BH,
+                             N, sc, stages, stream);
 }
 
 }  // namespace fa

@@ -15,6 +15,17 @@ hipError_t launch_fwd_f32(int d, bool causal, const float* q, const float* k, co
 hipError_t launch_fwd_fp8(int d, bool causal, const void* q8, const void* k8, const void* v8,
                           float qk_scale, float v_descale, void* o, float* lse, int BH, int N,
                           hipStream_t stream);
+// Factors of the backward passes: exponent factor c (P = 2^(s c - LSE log2 e)
+// for the raw product s of the operands), multipliers of the dK and dQ
+// outputs, and of the row terms D. Plain use: {scale log2 e, scale, scale, 1}.
+struct BwdScales {
+    float c, dk_mul, dq_mul, d_mul;
+};
+hipError_t launch_bwd_scaled(int dtype, int d, bool causal, const void* q, const void* k,
+                             const void* v, const void* o, const float* lse, const void* dO,
+                             void* dq, void* dk, void* dv, float* delta, float* lse2, int BH,
+                             int N, const BwdScales& sc, int stages, hipStream_t stream);
+hipError_t launch_e4m3_to_bf16(const void* src, void* dst, size_t n, hipStream_t stream);
 hipError_t launch_bwd(int dtype, int d, bool causal, const void* q, const void* k, const void* v,
                       const void* o, const float* lse, const void* dO, void* dq, void* dk,
                       void* dv, float* delta, float* lse2, int BH, int N, float scale,

@@ -24,6 +24,8 @@
  *    caller. The library allocates no memory and keeps no per-call state.
  *  - Layout: contiguous row-major [B, H, N, d] for Q, K, V, O, dO, dQ, dK, dV;
  *    LSE is [B, H, N] float32 (natural log, of the scaled scores).
+ *  - Alignment: every [.., N, d] tensor starts on a 16-byte boundary, every
+ *    float32 row-statistics array on a 4-byte one (FA_ERR_ARG otherwise).
  *  - d must be 64 or 128 (the 16-bit fa_fwd and fa_bwd also take 256).
  *    B, H, N >= 1 and B*H*N*d < 2^31.
  *  - causal != 0: query i attends to keys 0..i (the mask is not on the pages;
@@ -241,6 +243,36 @@ size_t fa_std_workspace_bytes(int B, int H, int N, int d);
 int fa_std_fwd(int dtype, const void* q, const void* k, const void* v, void* o,
                void* workspace, size_t workspace_bytes,
                int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/*
+ * Size in bytes of the scratch buffer fa_bwd_fp8 needs: bfloat16 copies of
+ * the Q, K, V codes plus fa_bwd's own scratch. Returns 0 for invalid shapes.
+ */
+size_t fa_bwd_fp8_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * Backward pass for fp8 inputs: gradients of L = <O, dO> with respect to the
+ * dequantised inputs Q = q_descale * q8 (and likewise K, V), where O and LSE
+ * come from fa_fwd_fp8 with the same arguments. The E4M3 codes are widened
+ * to bfloat16 (exactly) into the workspace and the 16-bit passes run on the
+ * codes with the descales folded into their factors: the exponent uses
+ * scale * q_descale * k_descale, the row terms D are divided by v_descale, dK
+ * is multiplied by scale * q_descale * v_descale and dQ by
+ * scale * k_descale * v_descale ("11.11 Flash Attention", sections "Flash
+ * Attention 3" (FP8) and "The Recomputation Trade-off"; the backward
+ * equations are those of fa_bwd).
+ *   q8, k8, v8      [B,H,N,d] OCP E4M3 codes (uint8), read only.
+ *   *_descale       > 0 and finite.
+ *   o_bf16, dO_bf16 [B,H,N,d] bfloat16;  lse [B,H,N] float32.
+ *   dq, dk, dv      [B,H,N,d] bfloat16, written.
+ *   workspace       at least fa_bwd_fp8_workspace_bytes(B,H,N,d) bytes,
+ *                   256-byte aligned; overwritten.
+ *   d               64, 128 or 256.
+ */
+int fa_bwd_fp8(const void* q8, const void* k8, const void* v8, float q_descale, float k_descale,
+               float v_descale, const void* o_bf16, const float* lse, const void* dO_bf16,
+               void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B,
+               int H, int N, int d, float scale, int causal, hipStream_t stream);
 
 /* Human-readable text for a fa_status value (static storage, never NULL). */
 const char* fa_status_string(int status);

@@ -239,3 +239,49 @@ def test_v1_workspace_and_validation(lib):
     assert v1(scale=0.0) == -7
     assert v1(wsb=need - 1) == -5
     assert v1(ws=ctypes.c_void_p(0x10040)) == -5
+
+
+def test_misaligned_pointers_rejected(lib):
+    odd = ctypes.c_void_p(0x1008)   # 8-byte but not 16-byte aligned
+    assert fwd(lib, q=odd) == -7
+    assert fwd(lib, o=odd) == -7
+    assert fwd(lib, lse=ctypes.c_void_p(0x1002)) == -7
+    assert lib.fa_fwd_fp8(odd, FAKE, FAKE, 1.0, 1.0, 1.0, FAKE, FAKE, 1, 1, 64, 128, 0.1, 0,
+                          None) == -7
+    need = fa.fa_bwd_workspace_bytes(1, 1, 64, 64)
+    assert lib.fa_bwd(fa.FA_BF16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, odd, FAKE,
+                      ctypes.c_void_p(0x10000), need, 1, 1, 64, 64, 0.1, 0, None) == -7
+
+
+def test_bwd_fp8_workspace_bytes(lib):
+    B, H, N, d = 1, 2, 100, 128
+    codes = -(-B * H * N * d * 2 // 256) * 256          # one bf16 copy, padded to 256 B
+    assert fa.fa_bwd_fp8_workspace_bytes(B, H, N, d) == 3 * codes + \
+        fa.fa_bwd_workspace_bytes(B, H, N, d)
+    assert fa.fa_bwd_fp8_workspace_bytes(B, H, N, 96) == 0
+    assert fa.fa_bwd_fp8_workspace_bytes(0, H, N, d) == 0
+
+
+def test_bwd_fp8_validation(lib):
+    B, H, N, d = 1, 2, 64, 128
+    need = fa.fa_bwd_fp8_workspace_bytes(B, H, N, d)
+
+    def f8b(**kw):
+        a = dict(q=FAKE, sq=1.0, sk=1.0, sv=1.0, ws=ctypes.c_void_p(0x100000), wsb=need, d=d,
+                 scale=0.1, dq=FAKE)
+        a.update(kw)
+        return lib.fa_bwd_fp8(a["q"], FAKE, FAKE, a["sq"], a["sk"], a["sv"], FAKE, FAKE, FAKE,
+                              a["dq"], FAKE, FAKE, a["ws"], a["wsb"], B, H, N, a["d"],
+                              a["scale"], 1, None)
+
+    assert f8b(q=None) == -1
+    assert f8b(dq=None) == -1
+    assert f8b(ws=None) == -1
+    assert f8b(d=96) == -4
+    assert f8b(sq=0.0) == -7
+    assert f8b(sv=float("inf")) == -7
+    assert f8b(sv=1e-39) == -7          # 1 / v_descale overflows
+    assert f8b(scale=-1.0) == -7
+    assert f8b(dq=ctypes.c_void_p(0x1004)) == -7
+    assert f8b(wsb=need - 1) == -5
+    assert f8b(ws=ctypes.c_void_p(0x100080)) == -5
