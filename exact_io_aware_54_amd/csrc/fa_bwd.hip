@@ -10,7 +10,7 @@
 //   dQ  = scale dS K,  dK = scale dS^T Q.
 //
 // Three launches on the caller's stream:
-//  1. bwd_pre: per row, D_i (fp32) and LSE_i * log2(e) into the workspace.
+//  1. bwd_pre: per row, -D_i (fp32) and LSE_i * log2(e) into the workspace.
 //  2. bwd_dkdv: one workgroup of eight wavefronts per (batch*head, block of
 //     128 keys), walking the query blocks of 64 rows (causal: from the
 //     diagonal on). K and V of the block stay in LDS; each wave owns 32 keys x
@@ -70,7 +70,7 @@ bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO, const float* _
 #pragma unroll
     for (int off = TPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, TPR);
     if (row < rows && part == 0) {
-        delta[row] = s * d_mul;
+        delta[row] = -(s * d_mul);  // stored negated: it seeds the dP accumulators
         lse2[row] = lse[row] * kLog2e;
     }
 }
@@ -125,7 +125,7 @@ struct DkdvWave {
         c = c_;
         tid = threadIdx.x;
         lane = tid & 63;
-        wave = tid >> 6;
+        wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches below
         l32 = lane & 31;
         h = lane >> 5;
         kg = wave & 3;
@@ -192,6 +192,33 @@ struct DkdvWave {
         if (wave == 1) __builtin_amdgcn_global_load_lds(delh + r, sDd, 4, 0, 0);
     }
 
+    // P = 2^(s c - LSE2), dS = P (dP - D) with pacc already holding dP - D;
+    // masked entries get P = 0
+    template <bool MASK>
+    __device__ __forceinline__ void softmax(f32x16& sacc, f32x16& pacc, const float* sL,
+                                            int qb0) const {
+        const int lo = key - qb0 - 4 * h;   // causal-visible iff const(r) >= lo
+        const int hi = N - qb0 - 4 * h;     // query < N iff const(r) < hi
+        const bool kvalid = key < N;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 lq = *reinterpret_cast<const f32x4*>(sL + 32 * qs + 8 * r4 + 4 * h);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * r4 + i;
+                float l2 = lq[i];
+                if (MASK) {
+                    const int cr = 8 * r4 + i;
+                    const bool vis = kvalid && cr < hi && (!CAUSAL || cr >= lo);
+                    if (!vis) l2 = INFINITY;
+                }
+                const float p = fast_exp2(fmaf(sacc[r], c, -l2));
+                sacc[r] = p;
+                pacc[r] = p * pacc[r];
+            }
+        }
+    }
+
     __device__ __forceinline__ void step(int ib, int nqb, const char* sK, const char* sV,
                                          const char* sQ, const char* sG, const float* sL,
                                          const float* sD, char* nQ, char* nG, float* nL,
@@ -203,8 +230,15 @@ struct DkdvWave {
         const int qb0 = qbase + 32 * qs;  // first query of this wave's subtile
         if (CAUSAL && key0 > qb0 + 31) return;  // every query of the subtile precedes every key
 
-        // S = Q K^T and dP = dO V^T (lane = key, register r = query qb0 + acc_row(r, h))
-        f32x16 sacc = f32x16{}, pacc = f32x16{};
+        // S = Q K^T and dP - D = dO V^T - D (lane = key, register r = query
+        // qb0 + acc_row(r, h)); the dP accumulators start from -D of their query
+        f32x16 sacc = f32x16{}, pacc;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 nd = *reinterpret_cast<const f32x4*>(sD + 32 * qs + 8 * r4 + 4 * h);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pacc[4 * r4 + i] = nd[i];
+        }
 #pragma unroll
         for (int s = 0; s < C::KS; ++s) {
             const V8 aq = *reinterpret_cast<const V8*>(sQ + roff[s]);
@@ -215,28 +249,12 @@ struct DkdvWave {
             pacc = mfma32(ag, bv, pacc);
         }
         const bool need_mask = key0 + 31 >= N || qb0 + 31 >= N || (CAUSAL && key0 + 31 > qb0);
-        const int lo = key - qb0 - 4 * h;   // causal-visible iff const(r) >= lo
-        const int hi = N - qb0 - 4 * h;     // query < N iff const(r) < hi
-        const bool kvalid = key < N;
-        // P = 2^(s c - LSE2), dS = P (dP - D); masked entries get P = 0
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-            const f32x4 lq = *reinterpret_cast<const f32x4*>(sL + 32 * qs + 8 * r4 + 4 * h);
-            const f32x4 dq = *reinterpret_cast<const f32x4*>(sD + 32 * qs + 8 * r4 + 4 * h);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 4 * r4 + i;
-                float l2 = lq[i];
-                if (need_mask) {
-                    const int cr = 8 * r4 + i;
-                    const bool vis = kvalid && cr < hi && (!CAUSAL || cr >= lo);
-                    if (!vis) l2 = INFINITY;
-                }
-                const float p = fast_exp2(fmaf(sacc[r], c, -l2));
-                sacc[r] = p;
-                pacc[r] = p * (pacc[r] - dq[i]);
-            }
-        }
+        // wave-uniform: only the diagonal and ragged-edge steps pay for the
+        // per-element mask
+        if (need_mask)
+            softmax<true>(sacc, pacc, sL, qb0);
+        else
+            softmax<false>(sacc, pacc, sL, qb0);
         V8 pf[2], sf[2];
         pf[0] = pack8<T>(sacc, 0);
         pf[1] = pack8<T>(sacc, 8);
@@ -312,12 +330,17 @@ bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
                 const float* __restrict__ delta, T* __restrict__ dK, T* __restrict__ dV, int BH,
                 int N, int nkb, float scale, float c) {
     using C = DkdvTile<D>;
+    // The Q / dO tiles (more strictly aligned, so the compiler places them
+    // first) sit below 64 KiB of LDS: the per-step reads then carry the
+    // buffer base in the instruction's immediate offset instead of a VALU add.
+    __shared__ __attribute__((aligned(4096))) char sQG0[2 * C::QTILEB];
+    __shared__ __attribute__((aligned(4096))) char sQG1[2 * C::QTILEB];
     __shared__ __attribute__((aligned(1024))) char sK[C::KTILEB];
     __shared__ __attribute__((aligned(1024))) char sV[C::KTILEB];
-    __shared__ __attribute__((aligned(1024))) char sQ0[C::QTILEB];
-    __shared__ __attribute__((aligned(1024))) char sQ1[C::QTILEB];
-    __shared__ __attribute__((aligned(1024))) char sG0[C::QTILEB];
-    __shared__ __attribute__((aligned(1024))) char sG1[C::QTILEB];
+    char* const sQ0 = sQG0;
+    char* const sG0 = sQG0 + C::QTILEB;
+    char* const sQ1 = sQG1;
+    char* const sG1 = sQG1 + C::QTILEB;
     __shared__ __attribute__((aligned(256))) float sL0[C::BM];
     __shared__ __attribute__((aligned(256))) float sL1[C::BM];
     __shared__ __attribute__((aligned(256))) float sD0[C::BM];
@@ -481,7 +504,7 @@ struct Dkdv1Wave {
                     if (!vis) l2 = INFINITY;
                 }
                 const float p = fast_exp2(fmaf(sacc[r], c, -l2));
-                if (DK) pacc[r] = p * (pacc[r] - dq[i]);
+                if (DK) pacc[r] = p * (pacc[r] + dq[i]);  // dq holds -D
                 else sacc[r] = p;
             }
         }
@@ -576,7 +599,7 @@ struct DqWave {
     const T* Kh;
     const T* Vh;
     int N, nkt, tid, lane, wave, l32, h, q0, qrow;
-    float c, lse2, del;
+    float c, lse2, del;             // del: -D of this lane's query
     V8 qf[C::KS], gf[C::KS];        // B operands: Q and dO rows of this lane's query
     int ld_row[C::NLOAD], ld_col[C::NLOAD];
     int roff[2][C::KS];             // 16-byte row reads of K / V (key 32 c2 + l32)
@@ -684,7 +707,7 @@ struct DqWave {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const float p = fast_exp2(fmaf(s[c2][r], c, -lse2));
-                dp[c2][r] = p * (dp[c2][r] - del);
+                dp[c2][r] = p * (dp[c2][r] + del);  // del holds -D
             }
         V8 sf[4];
         sf[0] = pack8<T>(dp[0], 0);
