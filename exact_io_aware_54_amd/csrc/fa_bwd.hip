@@ -110,6 +110,7 @@ struct DkdvWave {
     int N, tid, lane, wave, l32, h, kg, qs, key0, key;
     float c;
     int ldq_row[C::NLOADQ], ldq_col[C::NLOADQ];
+    unsigned ldq_off[C::NLOADQ];     // byte offset of this thread's 16 bytes within a full tile
     int roff[C::KS];                 // 16-byte row reads of Q / dO rows 32 qs + l32
     int koff[C::KS];                 // 16-byte row reads of K / V rows 32 kg + l32 (B operands)
     int toff[2][C::DB];              // transposing reads [half][b] (query group 0; +16 rows for g2 = 1)
@@ -138,6 +139,7 @@ struct DkdvWave {
             const int r = byte / C::ROWB, p = (byte % C::ROWB) / 16;
             ldq_row[i] = r;
             ldq_col[i] = (p ^ tile_swz<D>(r)) * 8;
+            ldq_off[i] = (unsigned)(r * D + ldq_col[i]) * 2u;
         }
 #pragma unroll
         for (int s = 0; s < C::KS; ++s) {
@@ -180,6 +182,21 @@ struct DkdvWave {
     // Q and dO rows [qbase, qbase + BM) and their LSE2 / D into one buffer set.
     __device__ __forceinline__ void issue(int qbase, char* sQd, char* sGd, float* sLd,
                                           float* sDd) const {
+        if (qbase + C::BM <= N) {  // whole tile in range: one add per 16-byte load pair
+            const unsigned base = (unsigned)qbase * (D * 2u);
+            const char* qb = reinterpret_cast<const char*>(Qh);
+            const char* gb = reinterpret_cast<const char*>(dOh);
+#pragma unroll
+            for (int i = 0; i < C::NLOADQ; ++i) {
+                const unsigned off = base + ldq_off[i];
+                const int o = i * (C::NT * 16) + wave * 1024;
+                __builtin_amdgcn_global_load_lds(qb + off, sQd + o, 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(gb + off, sGd + o, 16, 0, 0);
+            }
+            if (wave == 0) __builtin_amdgcn_global_load_lds(lse2h + qbase + lane, sLd, 4, 0, 0);
+            if (wave == 1) __builtin_amdgcn_global_load_lds(delh + qbase + lane, sDd, 4, 0, 0);
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < C::NLOADQ; ++i) {
             const size_t row = (size_t)min(qbase + ldq_row[i], N - 1) * D;
@@ -602,6 +619,7 @@ struct DqWave {
     float c, lse2, del;             // del: -D of this lane's query
     V8 qf[C::KS], gf[C::KS];        // B operands: Q and dO rows of this lane's query
     int ld_row[C::NLOAD], ld_col[C::NLOAD];
+    unsigned ld_off[C::NLOAD];      // byte offset of this thread's 16 bytes within a full tile
     int roff[2][C::KS];             // 16-byte row reads of K / V (key 32 c2 + l32)
     int toff[4][2][C::DB];          // transposing reads of K [g][half][b]
     f32x16 dqacc[C::DB];            // dQ^T: head dim in registers, query = lane
@@ -615,7 +633,7 @@ struct DqWave {
         c = c_;
         tid = threadIdx.x;
         lane = tid & 63;
-        wave = tid >> 6;
+        wave = __builtin_amdgcn_readfirstlane(tid >> 6);
         l32 = lane & 31;
         h = lane >> 5;
         q0 = qb * C::BM + 32 * wave;
@@ -638,6 +656,7 @@ struct DqWave {
             const int r = byte / C::ROWB, p = (byte % C::ROWB) / 16;
             ld_row[i] = r;
             ld_col[i] = (p ^ tile_swz<D>(r)) * 8;
+            ld_off[i] = (unsigned)(r * D + ld_col[i]) * 2u;
         }
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2)
@@ -661,6 +680,19 @@ struct DqWave {
     }
 
     __device__ __forceinline__ void issue(int kbase, char* sKd, char* sVd) const {
+        if (kbase + C::BN <= N) {  // whole tile in range: one add per 16-byte load pair
+            const unsigned base = (unsigned)kbase * (D * 2u);
+            const char* kb = reinterpret_cast<const char*>(Kh);
+            const char* vb = reinterpret_cast<const char*>(Vh);
+#pragma unroll
+            for (int i = 0; i < C::NLOAD; ++i) {
+                const unsigned off = base + ld_off[i];
+                const int o = i * (C::NT * 16) + wave * 1024;
+                __builtin_amdgcn_global_load_lds(kb + off, sKd + o, 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(vb + off, sVd + o, 16, 0, 0);
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < C::NLOAD; ++i) {
             const size_t row = (size_t)min(kbase + ld_row[i], N - 1) * D;

@@ -77,6 +77,7 @@ struct FwdWave {
     float c;
     V8 qf[C::KS];               // B operand of S^T = K Q^T (d = 16 s + 8 h + j)
     int ld_row[C::NLOAD], ld_col[C::NLOAD];
+    unsigned ld_off[C::NLOAD];  // byte offset of this thread's 16 bytes within a full tile
     int koff[C::KS];            // LDS byte offsets of the K operand reads (rows l32; +32 rows per subtile)
     int voff[2][C::DB];         // LDS byte offsets of the V^T transposing reads (key group 0; +16 rows per group)
     float m_run, l_run;         // running (reference) max of s * c and this lane's sum
@@ -111,6 +112,7 @@ struct FwdWave {
             const int r = byte / C::ROWB, p = (byte % C::ROWB) / 16;
             ld_row[i] = r;
             ld_col[i] = (p ^ tile_swz<D>(r)) * 8;
+            ld_off[i] = (unsigned)(r * D + ld_col[i]) * 2u;
         }
         // K (A side of S^T): key 32 c2 + l32, chunk 2 s + h. The swizzle repeats
         // every 16 rows, so subtile c2 is koff + 32 c2 rows.
@@ -134,6 +136,19 @@ struct FwdWave {
     }
 
     __device__ __forceinline__ void issue_tile(int kbase, char* sKd, char* sVd) const {
+        if (kbase + C::BN <= N) {  // whole tile in range: one add per 16-byte load pair
+            const unsigned base = (unsigned)kbase * (D * 2u);
+            const char* kb = reinterpret_cast<const char*>(Kh);
+            const char* vb = reinterpret_cast<const char*>(Vh);
+#pragma unroll
+            for (int i = 0; i < C::NLOAD; ++i) {
+                const unsigned off = base + ld_off[i];
+                const int o = i * (C::NT * 16) + wave * 1024;
+                __builtin_amdgcn_global_load_lds(kb + off, sKd + o, 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(vb + off, sVd + o, 16, 0, 0);
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < C::NLOAD; ++i) {
             const size_t row = (size_t)min(kbase + ld_row[i], N - 1) * D;
