@@ -481,6 +481,34 @@ struct Dkdv1Wave {
         if (DK && wave == 1) __builtin_amdgcn_global_load_lds(delh + r, sDd, 4, 0, 0);
     }
 
+    // P = 2^(s c - LSE2) into sacc, or dS = P (dP - D) into pacc (which holds
+    // dP - D); masked entries get P = 0. MODE 0: no mask, 1: mask, 2: mask
+    // if `masked` (one code path, no branch).
+    template <int MODE>
+    __device__ __forceinline__ void softmax(f32x16& sacc, f32x16& pacc, const float* sL,
+                                            int qbase, bool masked) const {
+        const int lo = key - qbase - 4 * h;   // causal-visible iff const(r) >= lo
+        const int hi = N - qbase - 4 * h;     // query < N iff const(r) < hi
+        const bool kvalid = key < N;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 lq = *reinterpret_cast<const f32x4*>(sL + 8 * r4 + 4 * h);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * r4 + i;
+                float l2 = lq[i];
+                if (MODE == 1 || (MODE == 2 && masked)) {
+                    const int cr = 8 * r4 + i;
+                    const bool vis = kvalid && cr < hi && (!CAUSAL || cr >= lo);
+                    if (!vis) l2 = INFINITY;
+                }
+                const float p = fast_exp2(fmaf(sacc[r], c, -l2));
+                if (DK) pacc[r] = p * pacc[r];
+                else sacc[r] = p;
+            }
+        }
+    }
+
     __device__ __forceinline__ void step(int ib, int nqb, const char* sQ, const char* sG,
                                          const float* sL, const float* sD, char* nQ, char* nG,
                                          float* nL, float* nD) {
@@ -490,8 +518,17 @@ struct Dkdv1Wave {
         if (ib + 1 < nqb) issue(qbase + C::BM, nQ, nG, nL, nD);
         if (CAUSAL && key0 > qbase + C::BM - 1) return;  // every query of the block precedes every key
 
-        // S = Q K^T (and dP = dO V^T): lane = key, register r = query qbase + acc_row(r, h)
+        // S = Q K^T (and dP - D = dO V^T - D, the dP accumulators starting from
+        // -D of their query): lane = key, register r = query qbase + acc_row(r, h)
         f32x16 sacc = f32x16{}, pacc = f32x16{};
+        if (DK) {
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const f32x4 nd = *reinterpret_cast<const f32x4*>(sD + 8 * r4 + 4 * h);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pacc[4 * r4 + i] = nd[i];
+            }
+        }
 #pragma unroll
         for (int s = 0; s < C::KS; ++s) {
             const int ro = tile_off<D>(l32, 16 * s + 8 * h);
@@ -502,29 +539,16 @@ struct Dkdv1Wave {
                 pacc = mfma32(ag, vf[DK ? s : 0], pacc);
             }
         }
+        // causal: a wave-uniform branch, so only diagonal and ragged-edge steps
+        // pay for the mask; non-causal keeps one path (a second one makes the
+        // dK launch spill)
         const bool need_mask = key0 + 31 >= N || qbase + 31 >= N || (CAUSAL && key0 + 31 > qbase);
-        const int lo = key - qbase - 4 * h;   // causal-visible iff const(r) >= lo
-        const int hi = N - qbase - 4 * h;     // query < N iff const(r) < hi
-        const bool kvalid = key < N;
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-            const f32x4 lq = *reinterpret_cast<const f32x4*>(sL + 8 * r4 + 4 * h);
-            const f32x4 dq = DK ? *reinterpret_cast<const f32x4*>(sD + 8 * r4 + 4 * h)
-                                : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 4 * r4 + i;
-                float l2 = lq[i];
-                if (need_mask) {
-                    const int cr = 8 * r4 + i;
-                    const bool vis = kvalid && cr < hi && (!CAUSAL || cr >= lo);
-                    if (!vis) l2 = INFINITY;
-                }
-                const float p = fast_exp2(fmaf(sacc[r], c, -l2));
-                if (DK) pacc[r] = p * (pacc[r] + dq[i]);  // dq holds -D
-                else sacc[r] = p;
-            }
-        }
+        if (!CAUSAL)
+            softmax<2>(sacc, pacc, sL, qbase, need_mask);
+        else if (need_mask)
+            softmax<1>(sacc, pacc, sL, qbase, true);
+        else
+            softmax<0>(sacc, pacc, sL, qbase, false);
         V8 op[2];
         op[0] = pack8<T>(DK ? pacc : sacc, 0);
         op[1] = pack8<T>(DK ? pacc : sacc, 8);
