@@ -427,6 +427,45 @@ def run_loop_order(path, torch, fa, inputs):
     out.close()
 
 
+def run_tile_sweep(path, torch, fa, inputs):
+    """The forward's two workgroup shapes (four and eight waves) on each bf16
+    forward workload, medians of 20 event-timed launches after 5 warm-ups."""
+    cases = [("C2", 4, 16, 2048, 64, False, 1002), ("C3a", 1, 32, 8192, 128, True, 1003),
+             ("C3b", 1, 32, 16384, 128, True, 1013), ("C4", 8, 16, 4096, 128, True, 1004),
+             ("non-causal", 2, 32, 8192, 128, False, 1005)]
+    out = open(path, "w")
+    for name, B, H, N, d, causal, seed in cases:
+        print(f"[tile-sweep] {name} B{B} H{H} N{N} d{d} causal={causal}", file=sys.stderr,
+              flush=True)
+        q, k, v = (t.cuda() for t in inputs.draw_qkv(B, H, N, d, seed, torch.bfloat16))
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), device="cuda", dtype=torch.float32)
+        flops = counted_flops(B, H, N, d, causal)
+        rec = {"workload": f"fwd bf16 {name} B{B} H{H} N{N} d{d} causal={causal}", "seed": seed,
+               "default_waves": 4 if (causal and N < 8192) else 8}
+        for waves in (4, 8):
+            fn = lambda: fa.fa_fwd_waves(q, k, v, o, lse, d ** -0.5, causal, waves)
+            for _ in range(5):
+                fn()
+            torch.cuda.synchronize()
+            times = []
+            for _ in range(20):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1))
+            med = sorted(times)[len(times) // 2]
+            rec[f"waves{waves}"] = {"median_ms": round(med, 4),
+                                    "tflops": round(flops / (med * 1e-3) / 1e12, 1)}
+        print(json.dumps(rec), file=out, flush=True)
+        print(f"[tile-sweep] {json.dumps(rec)}", file=sys.stderr, flush=True)
+        del q, k, v, o, lse
+        torch.cuda.empty_cache()
+    out.close()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -444,6 +483,9 @@ def main():
                     help="only run the IO-aware vs standard forward comparison, JSON lines to PATH")
     ap.add_argument("--compare-n", type=int, nargs="+", default=[2048, 8192, 32768],
                     help="sequence lengths of --compare-standard")
+    ap.add_argument("--tile-sweep", metavar="PATH",
+                    help="only time the forward's four- and eight-wave workgroup shapes on each "
+                         "bf16 forward workload, JSON lines to PATH")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device copy, the reference kernel for scaling "
                          "PMC byte counters")
@@ -454,7 +496,7 @@ def main():
               "communication, so the whole-job rate at N GPUs is N times the 1-GPU figure at "
               "the per-GPU head count; run with --gpus 1.", file=sys.stderr, flush=True)
         sys.exit(2)
-    if args.decode or args.compare_standard or args.loop_order:
+    if args.decode or args.compare_standard or args.loop_order or args.tile_sweep:
         import torch
         import exact_io_aware_54_amd as fa
         from exact_io_aware_54_amd import inputs
@@ -465,6 +507,8 @@ def main():
             run_decode(args.decode, torch, fa, inputs)
         if args.loop_order:
             run_loop_order(args.loop_order, torch, fa, inputs)
+        if args.tile_sweep:
+            run_tile_sweep(args.tile_sweep, torch, fa, inputs)
         if args.compare_standard:
             run_compare(args.compare_standard, torch, fa, inputs, args.compare_n)
         return

@@ -9,7 +9,7 @@ in the library's kernels; there is no fallback path. If the library has not
 been built, calls raise ``RuntimeError``.
 
 Entry points: ``fa_fwd``, ``fa_fwd_fp8``, ``fa_bwd``, ``fa_bwd_stage``,
-``fa_bwd_workspace_bytes``, ``fa_bwd_fp8``, ``fa_bwd_fp8_workspace_bytes``,
+``fa_bwd_workspace_bytes``, ``fa_fwd_waves``, ``fa_bwd_fp8``, ``fa_bwd_fp8_workspace_bytes``,
 ``fa_fwd_splitkv``,
 ``fa_fwd_splitkv_workspace_bytes``, ``fa_lse_merge``, ``fa_fwd_v1``,
 ``fa_fwd_v1_workspace_bytes``, ``fa_std_fwd``,
@@ -67,6 +67,8 @@ def load_library(path=None):
     lib.fa_fwd_splitkv.restype = i
     lib.fa_lse_merge.argtypes = [i, i, vp, vp, vp, vp, i, i, vp]
     lib.fa_lse_merge.restype = i
+    lib.fa_fwd_waves.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
+    lib.fa_fwd_waves.restype = i
     lib.fa_bwd_fp8_workspace_bytes.argtypes = [i, i, i, i]
     lib.fa_bwd_fp8_workspace_bytes.restype = sz
     lib.fa_bwd_fp8.argtypes = [vp, vp, vp, f, f, f, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f,
@@ -146,6 +148,20 @@ def fa_fwd(q, k, v, o, lse, scale, causal, stream=None):
     st = lib.fa_fwd(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                     B, H, N, d, float(scale), int(bool(causal)), _stream(stream))
     _raise("fa_fwd", st)
+
+
+def fa_fwd_waves(q, k, v, o, lse, scale, causal, waves, stream=None):
+    """fa_fwd with the workgroup shape forced: waves 0 (built-in), 4 or 8."""
+    import torch
+    lib = load_library()
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _check_bhnd(name, t, (B, H, N, d), q.dtype)
+    _check_bhnd("lse", lse, (B, H, N), torch.float32)
+    st = lib.fa_fwd_waves(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                          B, H, N, d, float(scale), int(bool(causal)), int(waves),
+                          _stream(stream))
+    _raise("fa_fwd_waves", st)
 
 
 def fa_fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, o, lse, scale, causal, stream=None):

@@ -98,7 +98,22 @@ int fa_fwd(int dtype, const void* q, const void* k, const void* v, void* o, floa
                                             static_cast<const float*>(v), static_cast<float*>(o),
                                             lse, BH, N, scale, stream));
     return status_of(
-        fa::launch_fwd_mfma(dtype, d, causal != 0, q, k, v, o, lse, BH, N, scale, stream));
+        fa::launch_fwd_mfma(dtype, d, causal != 0, q, k, v, o, lse, BH, N, scale, 0, stream));
+}
+
+int fa_fwd_waves(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int N, int d, float scale, int causal, int waves,
+                 hipStream_t stream) {
+    if (!q || !k || !v || !o) return FA_ERR_NULL;
+    if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+    const int st = check_shape(B, H, N, d, true);
+    if (st != FA_OK) return st;
+    if (!good_scale(scale)) return FA_ERR_ARG;
+    if (!aligned16(q, k, v, o) || !aligned4(lse)) return FA_ERR_ARG;
+    if (waves != 0 && waves != 4 && waves != 8) return FA_ERR_ARG;
+    if (d == 256 && waves == 8) return FA_ERR_ARG;
+    return status_of(fa::launch_fwd_mfma(dtype, d, causal != 0, q, k, v, o, lse, B * H, N, scale,
+                                         waves, stream));
 }
 
 int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, float q_descale, float k_descale,

@@ -298,15 +298,16 @@ hipError_t launch_nw(const void* q, const void* k, const void* v, void* o, float
     return hipGetLastError();
 }
 
-// Workgroup shape: eight waves (256 queries, one workgroup per CU, K/V tiles
-// shared by all eight) measured 5-6 % faster on non-causal and on causal
-// N >= 8192; four waves (128 queries, two workgroups per CU) are better for
-// shorter causal sequences, where 256-query blocks make the per-block work
-// too uneven.
+// Workgroup shape (waves = 0): eight waves (256 queries, one workgroup per
+// CU, K/V tiles shared by all eight) measured 5-6 % faster on non-causal and
+// on causal N >= 8192; four waves (128 queries, two workgroups per CU) are
+// better for shorter causal sequences, where 256-query blocks make the
+// per-block work too uneven. waves = 4 or 8 forces the shape.
 template <typename T, int D, bool CAUSAL>
 hipError_t launch_typed(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
-                        int N, float scale, hipStream_t stream) {
-    if (CAUSAL && N < 8192) return launch_nw<T, D, CAUSAL, 4>(q, k, v, o, lse, BH, N, scale, stream);
+                        int N, float scale, int waves, hipStream_t stream) {
+    if (waves == 0) waves = (CAUSAL && N < 8192) ? 4 : 8;
+    if (waves == 4) return launch_nw<T, D, CAUSAL, 4>(q, k, v, o, lse, BH, N, scale, stream);
     return launch_nw<T, D, CAUSAL, 8>(q, k, v, o, lse, BH, N, scale, stream);
 }
 
@@ -315,24 +316,25 @@ hipError_t launch_typed(const void* q, const void* k, const void* v, void* o, fl
 // accumulators in AGPRs.
 template <typename T>
 hipError_t launch_d(int d, bool causal, const void* q, const void* k, const void* v, void* o,
-                    float* lse, int BH, int N, float scale, hipStream_t stream) {
+                    float* lse, int BH, int N, float scale, int waves, hipStream_t stream) {
     if (d == 64)
-        return causal ? launch_typed<T, 64, true>(q, k, v, o, lse, BH, N, scale, stream)
-                      : launch_typed<T, 64, false>(q, k, v, o, lse, BH, N, scale, stream);
+        return causal ? launch_typed<T, 64, true>(q, k, v, o, lse, BH, N, scale, waves, stream)
+                      : launch_typed<T, 64, false>(q, k, v, o, lse, BH, N, scale, waves, stream);
     if (d == 256)
         return causal ? launch_nw<T, 256, true, 4>(q, k, v, o, lse, BH, N, scale, stream)
                       : launch_nw<T, 256, false, 4>(q, k, v, o, lse, BH, N, scale, stream);
-    return causal ? launch_typed<T, 128, true>(q, k, v, o, lse, BH, N, scale, stream)
-                  : launch_typed<T, 128, false>(q, k, v, o, lse, BH, N, scale, stream);
+    return causal ? launch_typed<T, 128, true>(q, k, v, o, lse, BH, N, scale, waves, stream)
+                  : launch_typed<T, 128, false>(q, k, v, o, lse, BH, N, scale, waves, stream);
 }
 
 }  // namespace
 
 hipError_t launch_fwd_mfma(int dtype, int d, bool causal, const void* q, const void* k,
                            const void* v, void* o, float* lse, int BH, int N, float scale,
-                           hipStream_t stream) {
-    if (dtype == 2) return launch_d<__bf16>(d, causal, q, k, v, o, lse, BH, N, scale, stream);
-    return launch_d<_Float16>(d, causal, q, k, v, o, lse, BH, N, scale, stream);
+                           int waves, hipStream_t stream) {
+    if (dtype == 2)
+        return launch_d<__bf16>(d, causal, q, k, v, o, lse, BH, N, scale, waves, stream);
+    return launch_d<_Float16>(d, causal, q, k, v, o, lse, BH, N, scale, waves, stream);
 }
 
 }  // namespace fa

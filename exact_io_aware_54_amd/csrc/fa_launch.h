@@ -7,9 +7,10 @@
 
 namespace fa {
 
+// waves: 0 = built-in workgroup shape, 4 or 8 = forced (d = 256 takes 4 only)
 hipError_t launch_fwd_mfma(int dtype, int d, bool causal, const void* q, const void* k,
                            const void* v, void* o, float* lse, int BH, int N, float scale,
-                           hipStream_t stream);
+                           int waves, hipStream_t stream);
 hipError_t launch_fwd_f32(int d, bool causal, const float* q, const float* k, const float* v,
                           float* o, float* lse, int BH, int N, float scale, hipStream_t stream);
 hipError_t launch_fwd_fp8(int d, bool causal, const void* q8, const void* k8, const void* v8,

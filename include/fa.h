@@ -82,6 +82,23 @@ int fa_fwd(int dtype, const void* q, const void* k, const void* v, void* o, floa
            int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
 
 /*
+ * fa_fwd for 16-bit inputs with the workgroup shape chosen by the caller, for
+ * tuning and for measuring the shapes against each other. Each workgroup
+ * takes a block of queries ("11.11 Flash Attention", section "Flash
+ * Attention 2": parallel over batch, heads and query blocks) and shares the
+ * K/V tiles it streams through LDS among its waves:
+ *   waves  0: the built-in choice (what fa_fwd runs);
+ *          4: four waves, 128 queries per workgroup, two workgroups per CU;
+ *          8: eight waves, 256 queries per workgroup, one workgroup per CU
+ *             (not at d = 256).
+ * Other arguments and errors as fa_fwd (fp32 gives FA_ERR_DTYPE); any other
+ * `waves` value gives FA_ERR_ARG. Results are identical for every shape.
+ */
+int fa_fwd_waves(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int N, int d, float scale, int causal, int waves,
+                 hipStream_t stream);
+
+/*
  * FP8 forward ("11.11 Flash Attention", section "Flash Attention 3": FP8
  * attention). Inputs are OCP FP8 E4M3 codes (1 byte each) with one float32
  * descale per tensor: the real value of Q is q8 * q_descale, and likewise for

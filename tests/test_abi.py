@@ -285,3 +285,20 @@ def test_bwd_fp8_validation(lib):
     assert f8b(dq=ctypes.c_void_p(0x1004)) == -7
     assert f8b(wsb=need - 1) == -5
     assert f8b(ws=ctypes.c_void_p(0x100080)) == -5
+
+
+def test_fwd_waves_validation(lib):
+    def fw(**kw):
+        a = dict(dtype=fa.FA_BF16, q=FAKE, d=128, waves=4, scale=0.1)
+        a.update(kw)
+        return lib.fa_fwd_waves(a["dtype"], a["q"], FAKE, FAKE, FAKE, FAKE, 1, 2, 64, a["d"],
+                                a["scale"], 1, a["waves"], None)
+    assert fw(q=None) == -1
+    assert fw(dtype=fa.FA_F32) == -3
+    assert fw(d=96) == -4
+    assert fw(waves=2) == -7
+    assert fw(waves=16) == -7
+    assert fw(waves=-1) == -7
+    assert fw(d=256, waves=8) == -7        # d = 256 runs four waves only
+    assert fw(scale=0.0) == -7
+    assert fw(q=ctypes.c_void_p(0x1008)) == -7
