@@ -8,14 +8,14 @@ and raises ``FAError`` on a non-zero status. Every step of the attention runs
 in the library's kernels; there is no fallback path. If the library has not
 been built, calls raise ``RuntimeError``.
 
-Entry points: ``fa_fwd``, ``fa_fwd_fp8``, ``fa_bwd``, ``fa_bwd_stage``,
-``fa_bwd_workspace_bytes``, ``fa_fwd_waves``, ``fa_bwd_fp8``, ``fa_bwd_fp8_workspace_bytes``,
-``fa_fwd_splitkv``,
+Entry points: ``fa_fwd``, ``fa_fwd_waves``, ``fa_fwd_fp8``, ``fa_bwd``,
+``fa_bwd_stage``, ``fa_bwd_workspace_bytes``, ``fa_bwd_fp8``,
+``fa_bwd_fp8_workspace_bytes``, ``fa_fwd_splitkv``,
 ``fa_fwd_splitkv_workspace_bytes``, ``fa_lse_merge``, ``fa_fwd_v1``,
-``fa_fwd_v1_workspace_bytes``, ``fa_std_fwd``,
-``fa_std_workspace_bytes``, ``fa_status_string``, ``fa_version``;
-``forward`` / ``backward`` / ``forward_fp8`` / ``backward_fp8`` / ``forward_splitkv`` /
-``forward_v1`` / ``forward_standard`` allocate outputs with torch and call them.
+``fa_fwd_v1_workspace_bytes``, ``fa_std_fwd``, ``fa_std_workspace_bytes``,
+``fa_status_string``, ``fa_version``; ``forward`` / ``backward`` /
+``forward_fp8`` / ``backward_fp8`` / ``forward_splitkv`` / ``forward_v1`` /
+``forward_standard`` allocate outputs with torch and call them.
 """
 
 import ctypes
