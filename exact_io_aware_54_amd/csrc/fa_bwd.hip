@@ -366,8 +366,11 @@ bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
                   "partial sums must fit the K/V and Q/dO tiles");
 
     const int L = xcd_remap(blockIdx.x, BH * nkb);
-    const int bh = L / nkb;
-    const int kb = L % nkb;  // causal: small kb has the most query blocks -> dispatched first
+    int bh = L / nkb, kb = L % nkb;
+    if (CAUSAL) {
+        causal_pair_order(L, nkb, BH, bh, kb);
+        kb = nkb - 1 - kb;  // small kb has the most query blocks
+    }
     const size_t head = (size_t)bh * N * D;
     const size_t rowbase = (size_t)bh * N;
 
@@ -601,8 +604,11 @@ bwd_dkdv1_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
     __shared__ __attribute__((aligned(256))) float sD1[64];
 
     const int L = xcd_remap(blockIdx.x, BH * nkb);
-    const int bh = L / nkb;
-    const int kb = L % nkb;
+    int bh = L / nkb, kb = L % nkb;
+    if (CAUSAL) {
+        causal_pair_order(L, nkb, BH, bh, kb);
+        kb = nkb - 1 - kb;  // small kb has the most query blocks
+    }
     const size_t head = (size_t)bh * N * D;
     const size_t rowbase = (size_t)bh * N;
 
@@ -807,8 +813,8 @@ bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
     __shared__ __attribute__((aligned(1024))) char sV1[C::TILEB];
 
     const int L = xcd_remap(blockIdx.x, BH * nqb);
-    const int bh = L / nqb;
-    const int qb = CAUSAL ? (nqb - 1 - L % nqb) : (L % nqb);
+    int bh = L / nqb, qb = L % nqb;
+    if (CAUSAL) causal_pair_order(L, nqb, BH, bh, qb);
     const size_t head = (size_t)bh * N * D;
     const size_t rowbase = (size_t)bh * N;
 

@@ -78,6 +78,24 @@ __device__ __forceinline__ int xcd_remap(int id, int G) {
     return x < tall ? x * per + loc : tall * per + (x - tall) * (per - 1) + loc;
 }
 
+// Causal order of (head, query block) for a remapped block id L: heads in
+// pairs, and within a pair the query blocks longest first, alternating
+// between the two heads. A causal query block's work grows with its index;
+// taking the long blocks of two heads before the short ones leaves no long
+// block for the end of the launch, while the K/V of the two heads (what the
+// running blocks of an XCD read) still fits that XCD's L2. An odd last head
+// is taken alone.
+__device__ __forceinline__ void causal_pair_order(int L, int nqb, int BH, int& bh, int& qb) {
+    const int pair = L / (2 * nqb), j = L - pair * 2 * nqb;
+    if (2 * pair + 1 < BH) {
+        bh = 2 * pair + (j & 1);
+        qb = nqb - 1 - (j >> 1);
+    } else {
+        bh = 2 * pair;
+        qb = nqb - 1 - j;
+    }
+}
+
 // When a 32x32 accumulator is reused as an MFMA operand, registers r..r+7 of
 // a lane in half h hold rows {4h..4h+3} and {8+4h..8+4h+3} of a 16-row group
 // (see acc_row). The other operand, read from LDS as 8 contiguous elements at

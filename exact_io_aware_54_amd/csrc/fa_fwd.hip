@@ -271,8 +271,8 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     __shared__ __attribute__((aligned(1024))) char sV1[C::TILEB];
 
     const int L = xcd_remap(blockIdx.x, BH * nqb);
-    const int bh = L / nqb;
-    const int qb = CAUSAL ? (nqb - 1 - L % nqb) : (L % nqb);
+    int bh = L / nqb, qb = L % nqb;
+    if (CAUSAL) causal_pair_order(L, nqb, BH, bh, qb);
     const size_t head = (size_t)bh * N * D;
 
     FwdWave<T, D, CAUSAL, NW> w;
