@@ -368,7 +368,7 @@ bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     const int L = xcd_remap(blockIdx.x, BH * nkb);
     int bh = L / nkb, kb = L % nkb;
     if (CAUSAL) {
-        causal_pair_order(L, nkb, BH, bh, kb);
+        causal_group_order(L, nkb, BH, bh, kb);
         kb = nkb - 1 - kb;  // small kb has the most query blocks
     }
     const size_t head = (size_t)bh * N * D;
@@ -606,7 +606,7 @@ bwd_dkdv1_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
     const int L = xcd_remap(blockIdx.x, BH * nkb);
     int bh = L / nkb, kb = L % nkb;
     if (CAUSAL) {
-        causal_pair_order(L, nkb, BH, bh, kb);
+        causal_group_order(L, nkb, BH, bh, kb);
         kb = nkb - 1 - kb;  // small kb has the most query blocks
     }
     const size_t head = (size_t)bh * N * D;
@@ -814,7 +814,7 @@ bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
 
     const int L = xcd_remap(blockIdx.x, BH * nqb);
     int bh = L / nqb, qb = L % nqb;
-    if (CAUSAL) causal_pair_order(L, nqb, BH, bh, qb);
+    if (CAUSAL) causal_group_order(L, nqb, BH, bh, qb);
     const size_t head = (size_t)bh * N * D;
     const size_t rowbase = (size_t)bh * N;
 

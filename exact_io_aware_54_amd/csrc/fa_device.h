@@ -79,21 +79,17 @@ __device__ __forceinline__ int xcd_remap(int id, int G) {
 }
 
 // Causal order of (head, query block) for a remapped block id L: heads in
-// pairs, and within a pair the query blocks longest first, alternating
-// between the two heads. A causal query block's work grows with its index;
-// taking the long blocks of two heads before the short ones leaves no long
-// block for the end of the launch, while the K/V of the two heads (what the
-// running blocks of an XCD read) still fits that XCD's L2. An odd last head
-// is taken alone.
-__device__ __forceinline__ void causal_pair_order(int L, int nqb, int BH, int& bh, int& qb) {
-    const int pair = L / (2 * nqb), j = L - pair * 2 * nqb;
-    if (2 * pair + 1 < BH) {
-        bh = 2 * pair + (j & 1);
-        qb = nqb - 1 - (j >> 1);
-    } else {
-        bh = 2 * pair;
-        qb = nqb - 1 - j;
-    }
+// groups of four, and within a group the query blocks longest first, taking
+// the four heads in turn. A causal query block's work grows with its index;
+// taking the long blocks of a few heads before the short ones leaves no long
+// block for the end of the launch, while the running blocks of an XCD still
+// read the K/V of only a few heads. A last group may hold fewer heads.
+__device__ __forceinline__ void causal_group_order(int L, int nqb, int BH, int& bh, int& qb) {
+    constexpr int G = 4;
+    const int grp = L / (G * nqb), j = L - grp * G * nqb;
+    const int h0 = grp * G, nh = min(G, BH - h0);
+    bh = h0 + j % nh;
+    qb = nqb - 1 - j / nh;
 }
 
 // When a 32x32 accumulator is reused as an MFMA operand, registers r..r+7 of

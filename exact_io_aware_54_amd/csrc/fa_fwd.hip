@@ -272,7 +272,7 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
 
     const int L = xcd_remap(blockIdx.x, BH * nqb);
     int bh = L / nqb, qb = L % nqb;
-    if (CAUSAL) causal_pair_order(L, nqb, BH, bh, qb);
+    if (CAUSAL) causal_group_order(L, nqb, BH, bh, qb);
     const size_t head = (size_t)bh * N * D;
 
     FwdWave<T, D, CAUSAL, NW> w;

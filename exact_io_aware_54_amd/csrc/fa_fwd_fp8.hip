@@ -53,8 +53,8 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
     __shared__ __attribute__((aligned(16))) uint8_t sV[2][F8_D * F8_VSTR];
 
     const int L = xcd_remap(blockIdx.x, BH * nqb);
-    const int bh = L / nqb;
-    const int qb = CAUSAL ? (nqb - 1 - L % nqb) : (L % nqb);
+    int bh = L / nqb, qb = L % nqb;
+    if (CAUSAL) causal_group_order(L, nqb, BH, bh, qb);
     const size_t head = (size_t)bh * N * F8_D;
     const uint8_t* Qh = Q + head;
     const uint8_t* Kh = K + head;
