@@ -625,11 +625,11 @@ bwd_dkdv1_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
 }
 
 // ---------------------------------------------------------------- 3. dQ
-template <int D>
+template <int D, int NW>
 struct DqTile {
-    static constexpr int BM = 128;               // queries per workgroup (4 waves x 32)
+    static constexpr int BM = 32 * NW;           // queries per workgroup (NW waves x 32)
     static constexpr int BN = 64;                // keys per tile
-    static constexpr int NT = 256;
+    static constexpr int NT = 64 * NW;
     static constexpr int ROWB = 2 * D;
     static constexpr int TILEB = BN * ROWB;
     static constexpr int NLOAD = TILEB / (NT * 16);
@@ -637,9 +637,9 @@ struct DqTile {
     static constexpr int DB = D / 32;
 };
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, int NW>
 struct DqWave {
-    using C = DqTile<D>;
+    using C = DqTile<D, NW>;
     using V8 = typename Vec<T>::x8;
     using V4 = typename Vec<T>::x4;
 
@@ -800,13 +800,13 @@ struct DqWave {
     }
 };
 
-template <typename T, int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, D > 128 ? 1 : 2)
+template <typename T, int D, bool CAUSAL, int NW>
+__global__ void __launch_bounds__(64 * NW, (D > 128 || NW == 8) ? 1 : 2)
 bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
               const T* __restrict__ dO, const float* __restrict__ lse2,
               const float* __restrict__ delta, T* __restrict__ dQ, int BH, int N, int nqb,
               float scale, float c) {
-    using C = DqTile<D>;
+    using C = DqTile<D, NW>;
     __shared__ __attribute__((aligned(1024))) char sK0[C::TILEB];
     __shared__ __attribute__((aligned(1024))) char sK1[C::TILEB];
     __shared__ __attribute__((aligned(1024))) char sV0[C::TILEB];
@@ -818,7 +818,7 @@ bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
     const size_t head = (size_t)bh * N * D;
     const size_t rowbase = (size_t)bh * N;
 
-    DqWave<T, D, CAUSAL> w;
+    DqWave<T, D, CAUSAL, NW> w;
     w.init(Q + head, K + head, V + head, dO + head, lse2 + rowbase, delta + rowbase, N, qb, c);
     w.issue(0, sK0, sV0);
     for (int kt = 0; kt < w.nkt; kt += 2) {
@@ -866,10 +866,21 @@ hipError_t launch_typed(const void* q, const void* k, const void* v, const void*
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (stages & 4) {
-        const int nqb = (N + DqTile<D>::BM - 1) / DqTile<D>::BM;
-        hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3(BH * nqb), dim3(256), 0, stream,
-                           tq, tk, tv, tdo, lse2, delta, static_cast<T*>(dq), BH, N, nqb,
-                           sc.dq_mul, c);
+        // eight waves (256 queries, K/V tiles shared by twice as many waves)
+        // once the launch has at least one such workgroup per CU; four below
+        // that, and always at d = 256 (one wave per SIMD)
+        constexpr int NW8 = D > 128 ? 4 : 8;
+        const int nqb8 = (N + DqTile<D, NW8>::BM - 1) / DqTile<D, NW8>::BM;
+        if (D <= 128 && (int64_t)BH * nqb8 >= 256) {
+            hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, NW8>), dim3(BH * nqb8),
+                               dim3(DqTile<D, NW8>::NT), 0, stream, tq, tk, tv, tdo, lse2, delta,
+                               static_cast<T*>(dq), BH, N, nqb8, sc.dq_mul, c);
+        } else {
+            const int nqb = (N + DqTile<D, 4>::BM - 1) / DqTile<D, 4>::BM;
+            hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, 4>), dim3(BH * nqb),
+                               dim3(DqTile<D, 4>::NT), 0, stream, tq, tk, tv, tdo, lse2, delta,
+                               static_cast<T*>(dq), BH, N, nqb, sc.dq_mul, c);
+        }
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return e;
