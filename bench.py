@@ -6,6 +6,12 @@ Workload (one "step"): fa_fwd then the three launches of the backward
 with inputs already resident in HBM. Counted FLOPs: 4*B*H*N^2*d for the
 forward, halved for causal, and 2.5x that for the backward.
 
+The GPU's clocks ramp up over the first steps after the idle input
+preparation (measured: the first step takes ~5 ms, steps settle at ~2.5 ms
+after about 15 of them), so the default warm-up is 30 steps and the timed
+region (50 steps) measures the steady state. The per-workload timings below
+warm up for at least 60 ms of GPU work for the same reason.
+
 Prints ONE JSON line on stdout. Besides the contract fields it carries
   roofline     -- for the kernel with the largest average duration, its
                   counted FLOPs / its HIP-event-timed duration against the
@@ -17,7 +23,7 @@ Prints ONE JSON line on stdout. Besides the contract fields it carries
 `--suite PATH` additionally times every workload of the parity suite and
 writes one JSON line per workload to PATH.
 `--decode PATH` runs only the split-KV (few queries, many keys) workloads and
-writes one JSON line per workload (median of 20 after 5 warm-ups; HBM rate
+writes one JSON line per workload (median of 20 after the warm-up; HBM rate
 from the bytes of Q, K, V and O read or written once).
 `--loop-order PATH` runs only the loop-order ablation: the first-generation
 order (fa_fwd_v1: K/V blocks outer, one workgroup per head, O / m / l through
@@ -105,6 +111,20 @@ def cpu_baseline(q, k, v, do, scale, causal, budget_s, max_heads=96):
     return {"value": flops / secs / 1e12, "unit": "TFLOPS", "cores": cores, "kind": "oracle",
             "sample": f"fwd+bwd of {done} whole heads (N={N}, d={d}, causal) of the same "
                       f"workload in float64 numpy, {secs:.1f} s"}
+
+
+def warm_up(fn, torch, min_ms=60.0, min_calls=5):
+    """Call `fn` until at least `min_calls` calls and `min_ms` of GPU time have run."""
+    total, calls = 0.0, 0
+    while calls < min_calls or total < min_ms:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        total += e0.elapsed_time(e1)
+        calls += 1
+    return calls
 
 
 def time_launches(fns, steps, warmup, torch):
@@ -211,7 +231,7 @@ def run_main(args):
 
 
 def run_suite(path, torch, fa, inputs):
-    """Median and minimum of 20 timed launches (after 5 warm-ups) for every workload."""
+    """Median and minimum of 20 timed launches (after at least 60 ms of warm-up) for every workload."""
     import statistics
     cases = [
         ("fwd bf16 B4 H16 N2048 d64", "fwd", torch.bfloat16, 4, 16, 2048, 64, False, "fwd_bf16"),
@@ -258,9 +278,7 @@ def run_suite(path, torch, fa, inputs):
                 fn = lambda: fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, scale, causal)  # noqa
                 flops = counted_flops(B, H, N, d, causal, backward=True)
             peak = PEAK_BF16_TFLOPS
-        for _ in range(5):
-            fn()
-        torch.cuda.synchronize()
+        warm_up(fn, torch)
         times = []
         for _ in range(20):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -355,9 +373,7 @@ def run_decode(path, torch, fa, inputs):
         ws = torch.empty(fa.fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, 0), device="cuda",
                          dtype=torch.uint8)
         fn = lambda: fa.fa_fwd_splitkv(q, k, v, o, lse, ws, d ** -0.5, causal, 0)  # noqa: E731
-        for _ in range(5):
-            fn()
-        torch.cuda.synchronize()
+        warm_up(fn, torch)
         times = []
         for _ in range(20):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -429,7 +445,7 @@ def run_loop_order(path, torch, fa, inputs):
 
 def run_tile_sweep(path, torch, fa, inputs):
     """The forward's two workgroup shapes (four and eight waves) on each bf16
-    forward workload, medians of 20 event-timed launches after 5 warm-ups."""
+    forward workload, medians of 20 event-timed launches after the warm-up."""
     cases = [("C2", 4, 16, 2048, 64, False, 1002), ("C3a", 1, 32, 8192, 128, True, 1003),
              ("C3b", 1, 32, 16384, 128, True, 1013), ("C4", 8, 16, 4096, 128, True, 1004),
              ("non-causal", 2, 32, 8192, 128, False, 1005)]
@@ -445,9 +461,7 @@ def run_tile_sweep(path, torch, fa, inputs):
                "default_waves": 4 if (causal and N < 8192) else 8}
         for waves in (4, 8):
             fn = lambda: fa.fa_fwd_waves(q, k, v, o, lse, d ** -0.5, causal, waves)
-            for _ in range(5):
-                fn()
-            torch.cuda.synchronize()
+            warm_up(fn, torch)
             times = []
             for _ in range(20):
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -469,8 +483,8 @@ def run_tile_sweep(path, torch, fa, inputs):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget for the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
