@@ -79,13 +79,16 @@ __device__ __forceinline__ int xcd_remap(int id, int G) {
 }
 
 // Causal order of (head, query block) for a remapped block id L: heads in
-// groups of four, and within a group the query blocks longest first, taking
-// the four heads in turn. A causal query block's work grows with its index;
-// taking the long blocks of a few heads before the short ones leaves no long
-// block for the end of the launch, while the running blocks of an XCD still
-// read the K/V of only a few heads. A last group may hold fewer heads.
+// groups of G, and within a group the query blocks longest first, taking the
+// G heads in turn. A causal query block's work grows with its index; taking
+// the long blocks of a few heads before the short ones leaves no long block
+// for the end of the launch, while the running blocks of an XCD still read
+// the K/V of only a few heads. xcd_remap hands every XCD a contiguous range
+// of about BH/8 heads, so G = min(4, BH/8) keeps a group inside one XCD's
+// range (a group spread over two XCDs would give one of them all the long
+// blocks). A last group may hold fewer heads.
 __device__ __forceinline__ void causal_group_order(int L, int nqb, int BH, int& bh, int& qb) {
-    constexpr int G = 4;
+    const int G = max(1, min(4, BH >> 3));
     const int grp = L / (G * nqb), j = L - grp * G * nqb;
     const int h0 = grp * G, nh = min(G, BH - h0);
     bh = h0 + j % nh;
