@@ -365,11 +365,14 @@ bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     static_assert(2 * C::PARTB <= C::KTILEB && C::PARTB <= C::QTILEB,
                   "partial sums must fit the K/V and Q/dO tiles");
 
-    const int L = xcd_remap(blockIdx.x, BH * nkb);
-    int bh = L / nkb, kb = L % nkb;
+    int bh, kb;
     if (CAUSAL) {
-        causal_group_order(L, nkb, BH, bh, kb);
+        causal_block(blockIdx.x, nkb, BH, bh, kb);
         kb = nkb - 1 - kb;  // small kb has the most query blocks
+    } else {
+        const int L = xcd_remap(blockIdx.x, BH * nkb);
+        bh = L / nkb;
+        kb = L % nkb;
     }
     const size_t head = (size_t)bh * N * D;
     const size_t rowbase = (size_t)bh * N;
@@ -603,11 +606,14 @@ bwd_dkdv1_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
     __shared__ __attribute__((aligned(256))) float sD0[64];
     __shared__ __attribute__((aligned(256))) float sD1[64];
 
-    const int L = xcd_remap(blockIdx.x, BH * nkb);
-    int bh = L / nkb, kb = L % nkb;
+    int bh, kb;
     if (CAUSAL) {
-        causal_group_order(L, nkb, BH, bh, kb);
+        causal_block(blockIdx.x, nkb, BH, bh, kb);
         kb = nkb - 1 - kb;  // small kb has the most query blocks
+    } else {
+        const int L = xcd_remap(blockIdx.x, BH * nkb);
+        bh = L / nkb;
+        kb = L % nkb;
     }
     const size_t head = (size_t)bh * N * D;
     const size_t rowbase = (size_t)bh * N;
@@ -812,9 +818,14 @@ bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
     __shared__ __attribute__((aligned(1024))) char sV0[C::TILEB];
     __shared__ __attribute__((aligned(1024))) char sV1[C::TILEB];
 
-    const int L = xcd_remap(blockIdx.x, BH * nqb);
-    int bh = L / nqb, qb = L % nqb;
-    if (CAUSAL) causal_group_order(L, nqb, BH, bh, qb);
+    int bh, qb;
+    if (CAUSAL) {
+        causal_block(blockIdx.x, nqb, BH, bh, qb);
+    } else {
+        const int L = xcd_remap(blockIdx.x, BH * nqb);
+        bh = L / nqb;
+        qb = L % nqb;
+    }
     const size_t head = (size_t)bh * N * D;
     const size_t rowbase = (size_t)bh * N;
 

@@ -78,21 +78,32 @@ __device__ __forceinline__ int xcd_remap(int id, int G) {
     return x < tall ? x * per + loc : tall * per + (x - tall) * (per - 1) + loc;
 }
 
-// Causal order of (head, query block) for a remapped block id L: heads in
-// groups of G, and within a group the query blocks longest first, taking the
-// G heads in turn. A causal query block's work grows with its index; taking
-// the long blocks of a few heads before the short ones leaves no long block
-// for the end of the launch, while the running blocks of an XCD still read
-// the K/V of only a few heads. xcd_remap hands every XCD a contiguous range
-// of about BH/8 heads, so G = min(4, BH/8) keeps a group inside one XCD's
-// range (a group spread over two XCDs would give one of them all the long
-// blocks). A last group may hold fewer heads.
-__device__ __forceinline__ void causal_group_order(int L, int nqb, int BH, int& bh, int& qb) {
-    const int G = max(1, min(4, BH >> 3));
-    const int grp = L / (G * nqb), j = L - grp * G * nqb;
-    const int h0 = grp * G, nh = min(G, BH - h0);
-    bh = h0 + j % nh;
-    qb = nqb - 1 - j / nh;
+// (head, query block) of causal block `id` (blockIdx.x). A causal query
+// block's work grows with its index, so each XCD should run its longest
+// blocks first and all XCDs should get the same total work. Block ids go to
+// the eight XCDs in turn.
+//  - BH a multiple of 8: xcd_remap hands every XCD BH/8 whole heads; within
+//    an XCD the heads go in groups of G (4, 2 or 1, dividing BH/8), each
+//    group's query blocks longest first with its heads taken in turn. Taking the long
+//    blocks of a few heads before the short ones leaves no long block for
+//    the end of the launch, while the running blocks of an XCD still read
+//    the K/V of only a few heads.
+//  - otherwise the XCD ranges would split heads and one XCD would get the
+//    long half of a head: the blocks are dealt instead, longest first over
+//    all heads, block id k being the k-th longest, so XCD x gets every
+//    eighth one.
+__device__ __forceinline__ void causal_block(int id, int nqb, int BH, int& bh, int& qb) {
+    if ((BH & 7) == 0) {
+        const int L = xcd_remap(id, BH * nqb);
+        const int hx = BH >> 3;  // heads per XCD
+        const int G = (hx & 3) == 0 ? 4 : (hx & 1) == 0 ? 2 : 1;
+        const int grp = L / (G * nqb), j = L - grp * G * nqb;
+        bh = grp * G + j % G;
+        qb = nqb - 1 - j / G;
+    } else {
+        bh = id % BH;
+        qb = nqb - 1 - id / BH;
+    }
 }
 
 // When a 32x32 accumulator is reused as an MFMA operand, registers r..r+7 of

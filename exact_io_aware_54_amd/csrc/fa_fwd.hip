@@ -270,9 +270,14 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     __shared__ __attribute__((aligned(1024))) char sV0[C::TILEB];
     __shared__ __attribute__((aligned(1024))) char sV1[C::TILEB];
 
-    const int L = xcd_remap(blockIdx.x, BH * nqb);
-    int bh = L / nqb, qb = L % nqb;
-    if (CAUSAL) causal_group_order(L, nqb, BH, bh, qb);
+    int bh, qb;
+    if (CAUSAL) {
+        causal_block(blockIdx.x, nqb, BH, bh, qb);
+    } else {
+        const int L = xcd_remap(blockIdx.x, BH * nqb);
+        bh = L / nqb;
+        qb = L % nqb;
+    }
     const size_t head = (size_t)bh * N * D;
 
     FwdWave<T, D, CAUSAL, NW> w;

@@ -52,9 +52,14 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
     __shared__ __attribute__((aligned(16))) uint8_t sK[2][F8_BN * F8_KSTR];
     __shared__ __attribute__((aligned(16))) uint8_t sV[2][F8_D * F8_VSTR];
 
-    const int L = xcd_remap(blockIdx.x, BH * nqb);
-    int bh = L / nqb, qb = L % nqb;
-    if (CAUSAL) causal_group_order(L, nqb, BH, bh, qb);
+    int bh, qb;
+    if (CAUSAL) {
+        causal_block(blockIdx.x, nqb, BH, bh, qb);
+    } else {
+        const int L = xcd_remap(blockIdx.x, BH * nqb);
+        bh = L / nqb;
+        qb = L % nqb;
+    }
     const size_t head = (size_t)bh * N * F8_D;
     const uint8_t* Qh = Q + head;
     const uint8_t* Kh = K + head;
