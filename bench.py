@@ -458,7 +458,7 @@ def run_tile_sweep(path, torch, fa, inputs):
         lse = torch.empty((B, H, N), device="cuda", dtype=torch.float32)
         flops = counted_flops(B, H, N, d, causal)
         rec = {"workload": f"fwd bf16 {name} B{B} H{H} N{N} d{d} causal={causal}", "seed": seed,
-               "default_waves": 4 if (causal and N < 8192) else 8}
+               "default_waves": 8 if B * H * ((N + 255) // 256) >= 256 else 4}
         for waves in (4, 8):
             fn = lambda: fa.fa_fwd_waves(q, k, v, o, lse, d ** -0.5, causal, waves)
             warm_up(fn, torch)
