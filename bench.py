@@ -32,8 +32,8 @@ fp16, N = 2048 and 8192, causal and not; and B=8 at N=2048, where the
 first-generation order has one workgroup per CU), one JSON line per case.
 `--compare-standard PATH` runs only the comparison of the IO-aware forward with
 the standard (materialising) forward that the pages' exercise describes
-(B=1, H=32, d=128, fp16 random normals, N = 2048, 8192, 32768; 3 warm-up and
-10 timed runs each; peak device memory from torch's allocator) and writes one
+(B=1, H=32, d=128, fp16 random normals, N = 2048, 8192, 32768; at least 60 ms
+of warm-up and 10 timed runs each; peak device memory from torch's allocator) and writes one
 JSON line per sequence length to PATH.
 """
 
@@ -322,9 +322,7 @@ def run_compare(path, torch, fa, inputs, lengths=(2048, 8192, 32768)):
                 ws = torch.empty(fa.fa_std_workspace_bytes(B, H, N, d), device="cuda",
                                  dtype=torch.uint8)
                 fn = lambda: fa.fa_std_fwd(q, k, v, o, ws, scale, False)  # noqa: E731
-            for _ in range(3):
-                fn()
-            torch.cuda.synchronize()
+            warm_up(fn, torch)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             for _ in range(10):
@@ -417,8 +415,7 @@ def run_loop_order(path, torch, fa, inputs):
         flops = counted_flops(B, H, N, d, causal)
         for name, fn in fns.items():
             reps = 3 if name == "v1_kv_outer" else 10
-            fn()
-            torch.cuda.synchronize()
+            warm_up(fn, torch)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             for _ in range(reps):
