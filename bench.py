@@ -19,6 +19,9 @@ Prints ONE JSON line on stdout. Besides the contract fields it carries
                   PMC summary if it was taken on the current kernel source;
   cpu_baseline -- the float64 CPU oracle timed on a bounded sample of heads
                   of the same workload (reported, never a target);
+  probe        -- the practical dense bf16 MFMA rate and the shader clock
+                  under that load, from fa_probe_mfma (the measured ceiling
+                  beside the spec peak);
   breakdown    -- per-launch times and TFLOPS.
 `--suite PATH` additionally times every workload of the parity suite and
 writes one JSON line per workload to PATH.
@@ -113,6 +116,35 @@ def cpu_baseline(q, k, v, do, scale, causal, budget_s, max_heads=96):
                       f"workload in float64 numpy, {secs:.1f} s"}
 
 
+def mfma_probe(torch, fa, blocks=512, iters=4096):
+    """The practical dense bf16 MFMA rate and the shader clock under that load
+    (fa_probe_mfma: 512 workgroups of four waves, two waves per SIMD, operands
+    in registers). Returns None if the probe cannot run."""
+    try:
+        sink = torch.zeros(3 * blocks, device="cuda", dtype=torch.int64)
+        run = lambda: fa.fa_probe_mfma(sink, blocks, iters)  # noqa: E731
+        warm_up(run, torch, min_ms=20.0, min_calls=3)
+        times = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            run()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        ms = sorted(times)[len(times) // 2]
+        flops = blocks * 4 * iters * 4 * 32768
+        v = sink.view(blocks, 3).cpu().double()
+        clk = sorted((v[:, 0] / v[:, 1]).tolist())[blocks // 2] * 100.0  # MHz
+        return {"mfma_bf16_tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                "sclk_mhz_under_mfma": round(clk, 0), "probe_ms": round(ms, 4),
+                "note": "dense 32x32x16 bf16 MFMAs from registers; clock = s_memtime / "
+                        "s_memrealtime ticks x 100 MHz (median over workgroups)"}
+    except Exception as exc:  # a missing probe must not hide the bench line
+        print(f"[bench] mfma probe failed: {exc}", file=sys.stderr, flush=True)
+        return None
+
+
 def warm_up(fn, torch, min_ms=60.0, min_calls=5):
     """Call `fn` until at least `min_calls` calls and `min_ms` of GPU time have run."""
     total, calls = 0.0, 0
@@ -198,6 +230,11 @@ def run_main(args):
                 "traffic": traffic_for(kname), "avg_launch_ms": round(kms, 4),
                 "counted_flops_per_launch": kflops}
 
+    probe = mfma_probe(torch, fa)
+    if probe is not None:
+        probe["value_frac_of_probe"] = round(value / probe["mfma_bf16_tflops"], 4)
+        roofline["frac_of_probe"] = round(achieved / probe["mfma_bf16_tflops"], 4)
+
     cpu = None
     if not args.no_cpu_baseline:
         print(f"[bench] cpu baseline (~{args.cpu_seconds:.0f} s of oracle work)", file=sys.stderr,
@@ -215,6 +252,7 @@ def run_main(args):
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "probe": probe,
         "breakdown": {
             "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
             "bwd_stage_ms": {"pre": round(pre_ms, 4), "dkdv": round(main_ms, 4),

@@ -13,7 +13,7 @@ Entry points: ``fa_fwd``, ``fa_fwd_waves``, ``fa_fwd_fp8``, ``fa_bwd``,
 ``fa_bwd_fp8_workspace_bytes``, ``fa_fwd_splitkv``,
 ``fa_fwd_splitkv_workspace_bytes``, ``fa_lse_merge``, ``fa_fwd_v1``,
 ``fa_fwd_v1_workspace_bytes``, ``fa_std_fwd``, ``fa_std_workspace_bytes``,
-``fa_status_string``, ``fa_version``; ``forward`` / ``backward`` /
+``fa_probe_mfma``, ``fa_status_string``, ``fa_version``; ``forward`` / ``backward`` /
 ``forward_fp8`` / ``backward_fp8`` / ``forward_splitkv`` / ``forward_v1`` /
 ``forward_standard`` allocate outputs with torch and call them.
 """
@@ -69,6 +69,8 @@ def load_library(path=None):
     lib.fa_lse_merge.restype = i
     lib.fa_fwd_waves.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
     lib.fa_fwd_waves.restype = i
+    lib.fa_probe_mfma.argtypes = [vp, i, i, vp]
+    lib.fa_probe_mfma.restype = i
     lib.fa_bwd_fp8_workspace_bytes.argtypes = [i, i, i, i]
     lib.fa_bwd_fp8_workspace_bytes.restype = sz
     lib.fa_bwd_fp8.argtypes = [vp, vp, vp, f, f, f, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f,
@@ -287,6 +289,15 @@ def fa_bwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, o, lse, do, dq, dk, 
                         _ptr(dv), _ptr(workspace), workspace.numel(), B, H, N, d, float(scale),
                         int(bool(causal)), _stream(stream))
     _raise("fa_bwd_fp8", st)
+
+
+def fa_probe_mfma(sink, blocks, iters, stream=None):
+    """Launch the MFMA-rate / clock probe; sink is an int64 device tensor of 3*blocks."""
+    import torch
+    if sink.dtype != torch.int64 or not sink.is_cuda or sink.numel() < 3 * blocks:
+        raise ValueError("sink must be an int64 device tensor of at least 3*blocks elements")
+    _raise("fa_probe_mfma", load_library().fa_probe_mfma(_ptr(sink), int(blocks), int(iters),
+                                                          _stream(stream)))
 
 
 def fa_fwd_v1_workspace_bytes(B, H, N, d):

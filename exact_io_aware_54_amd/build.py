@@ -13,7 +13,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa.so")
 
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd_f32.hip", "fa_fwd_fp8.hip", "fa_bwd.hip",
-           "fa_std.hip", "fa_splitkv.hip", "fa_v1.hip", "fa_convert.hip"]
+           "fa_std.hip", "fa_splitkv.hip", "fa_v1.hip", "fa_convert.hip", "fa_probe.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -220,6 +220,13 @@ int fa_bwd_fp8(const void* q8, const void* k8, const void* v8, float q_descale, 
                                            stream));
 }
 
+int fa_probe_mfma(unsigned long long* sink, int blocks, int iters, hipStream_t stream) {
+    if (!sink) return FA_ERR_NULL;
+    if (blocks < 1 || blocks > 65536 || iters < 1 || iters > (1 << 24)) return FA_ERR_ARG;
+    if (((uintptr_t)sink & 7) != 0) return FA_ERR_ARG;
+    return status_of(fa::launch_mfma_probe(sink, blocks, iters, stream));
+}
+
 size_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits) {
     if (splitkv_shape(B, H, Nq, Nk, d, num_splits) != FA_OK) return 0;
     const SplitPlan pl = splitkv_plan(B, H, Nq, Nk, num_splits);

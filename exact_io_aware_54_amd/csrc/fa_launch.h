@@ -27,6 +27,8 @@ hipError_t launch_bwd_scaled(int dtype, int d, bool causal, const void* q, const
                              void* dq, void* dk, void* dv, float* delta, float* lse2, int BH,
                              int N, const BwdScales& sc, int stages, hipStream_t stream);
 hipError_t launch_e4m3_to_bf16(const void* src, void* dst, size_t n, hipStream_t stream);
+hipError_t launch_mfma_probe(unsigned long long* sink, int blocks, int iters,
+                             hipStream_t stream);
 hipError_t launch_bwd(int dtype, int d, bool causal, const void* q, const void* k, const void* v,
                       const void* o, const float* lse, const void* dO, void* dq, void* dk,
                       void* dv, float* delta, float* lse2, int BH, int N, float scale,

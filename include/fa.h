@@ -291,6 +291,21 @@ int fa_bwd_fp8(const void* q8, const void* k8, const void* v8, float q_descale, 
                void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B,
                int H, int N, int d, float scale, int causal, hipStream_t stream);
 
+/*
+ * Measurement probe (not part of the attention computation): `blocks`
+ * workgroups of four waves each run `iters` rounds of four independent
+ * 32x32x16 bf16 MFMAs with operands in registers, i.e. 4 * 4 * iters * 32768
+ * FLOP per workgroup, at the chip's practical dense MFMA rate. For each
+ * workgroup it writes three values to sink[3*w .. 3*w+2]: elapsed shader
+ * clocks (s_memtime), elapsed ticks of the constant-rate real-time counter
+ * (s_memrealtime, 100 MHz on this GPU family) and a checksum. The caller
+ * times the launch for TFLOP/s; clocks / ticks * 100 MHz is the shader clock
+ * under dense MFMA load.
+ *   sink    device buffer of 3 * blocks uint64, 8-byte aligned, written.
+ *   blocks  1 .. 65536;  iters  1 .. 2^24 (FA_ERR_ARG otherwise).
+ */
+int fa_probe_mfma(unsigned long long* sink, int blocks, int iters, hipStream_t stream);
+
 /* Human-readable text for a fa_status value (static storage, never NULL). */
 const char* fa_status_string(int status);
 

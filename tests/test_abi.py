@@ -302,3 +302,11 @@ def test_fwd_waves_validation(lib):
     assert fw(d=256, waves=8) == -7        # d = 256 runs four waves only
     assert fw(scale=0.0) == -7
     assert fw(q=ctypes.c_void_p(0x1008)) == -7
+
+
+def test_probe_validation(lib):
+    assert lib.fa_probe_mfma(None, 4, 10, None) == -1
+    assert lib.fa_probe_mfma(FAKE, 0, 10, None) == -7
+    assert lib.fa_probe_mfma(FAKE, 4, 0, None) == -7
+    assert lib.fa_probe_mfma(FAKE, 65537, 10, None) == -7
+    assert lib.fa_probe_mfma(ctypes.c_void_p(0x1004), 4, 10, None) == -7
