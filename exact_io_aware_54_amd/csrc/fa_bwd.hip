@@ -656,9 +656,14 @@ struct DqWave {
     V8 qf[C::KS], gf[C::KS];        // B operands: Q and dO rows of this lane's query
     int ld_row[C::NLOAD], ld_col[C::NLOAD];
     unsigned ld_off[C::NLOAD];      // byte offset of this thread's 16 bytes within a full tile
-    int roff[2][C::KS];             // 16-byte row reads of K / V (key 32 c2 + l32)
-    int toff[4][2][C::DB];          // transposing reads of K [g][half][b]
+    int roff[C::KS];                // 16-byte row reads of K / V (key l32; +32 rows for c2 = 1)
+    int toff[2][C::DB];             // transposing reads of K [half][b] (g = 0; +16 g rows)
     f32x16 dqacc[C::DB];            // dQ^T: head dim in registers, query = lane
+    // -D of this lane's query in every register, the seed of the dP^T
+    // accumulators (saves the subtraction per element); kept where its 16
+    // registers fit without spilling
+    static constexpr bool SEED = D <= 64 || (D == 128 && NW == 8);
+    f32x16 dinit;
 
     __device__ __forceinline__ void init(const T* Qh, const T* Kh_, const T* Vh_, const T* dOh,
                                          const float* lse2h, const float* delh, int N_, int qb,
@@ -695,24 +700,23 @@ struct DqWave {
             ld_off[i] = (unsigned)(r * D + ld_col[i]) * 2u;
         }
 #pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-            for (int s = 0; s < C::KS; ++s) roff[c2][s] = tile_off<D>(32 * c2 + l32, 16 * s + 8 * h);
+        for (int s = 0; s < C::KS; ++s) roff[s] = tile_off<D>(l32, 16 * s + 8 * h);
         // transposing reads of K: this lane supplies key 16 g + 8 half + 4 h +
         // (lane % 16) / 4, head dims 32 b + 16 ((lane / 16) % 2) + 4 (lane % 4);
         // it receives head dim 32 b + lane % 32 at keys 16 g + 8 half + 4 h + 0..3,
         // the key order of registers 8 (g % 2) + 4 half + 0..3 of dS^T subtile g / 2.
         const int src_r = 4 * h + (lane & 15) / 4;
         const int src_d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+// the swizzle repeats every 16 rows: rows + 16 g are toff + 16 g rows
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
+        for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-                for (int b = 0; b < C::DB; ++b)
-                    toff[g][hf][b] = tile_off<D>(16 * g + 8 * hf + src_r, 32 * b + src_d);
+            for (int b = 0; b < C::DB; ++b)
+                toff[hf][b] = tile_off<D>(8 * hf + src_r, 32 * b + src_d);
 #pragma unroll
         for (int b = 0; b < C::DB; ++b) dqacc[b] = f32x16{};
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dinit[r] = SEED ? del : 0.f;
     }
 
     __device__ __forceinline__ void issue(int kbase, char* sKd, char* sVd) const {
@@ -750,14 +754,14 @@ struct DqWave {
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2) {
             s[c2] = f32x16{};
-            dp[c2] = f32x16{};
+            dp[c2] = dinit;
         }
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) {
-                const V8 ak = *reinterpret_cast<const V8*>(kb + roff[c2][ks]);
-                const V8 av = *reinterpret_cast<const V8*>(vb + roff[c2][ks]);
+                const V8 ak = *reinterpret_cast<const V8*>(kb + roff[ks] + c2 * 32 * C::ROWB);
+                const V8 av = *reinterpret_cast<const V8*>(vb + roff[ks] + c2 * 32 * C::ROWB);
                 s[c2] = mfma32(ak, qf[ks], s[c2]);
                 dp[c2] = mfma32(av, gf[ks], dp[c2]);
             }
@@ -775,7 +779,7 @@ struct DqWave {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const float p = fast_exp2(fmaf(s[c2][r], c, -lse2));
-                dp[c2][r] = p * (dp[c2][r] + del);  // del holds -D
+                dp[c2][r] = SEED ? p * dp[c2][r] : p * (dp[c2][r] + del);  // dP - D; del holds -D
             }
         V8 sf[4];
         sf[0] = pack8<T>(dp[0], 0);
@@ -786,7 +790,7 @@ struct DqWave {
         for (int g = 0; g < 4; ++g)
 #pragma unroll
             for (int b = 0; b < C::DB; ++b) {
-                const V8 a = tr_read8<V8>(kb, toff[g][0][b], toff[g][1][b]);
+                const V8 a = tr_read8<V8>(kb + g * 16 * C::ROWB, toff[0][b], toff[1][b]);
                 dqacc[b] = mfma32(a, sf[g], dqacc[b]);
             }
     }
