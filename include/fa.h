@@ -116,8 +116,9 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v8,
 
 /*
  * Size in bytes of the scratch buffer fa_bwd needs: two float32 vectors of
- * B*H*N entries, the row terms D_i = sum_k dO_ik O_ik and LSE_i * log2(e)
- * (each padded to 256 bytes). Returns 0 for invalid shapes.
+ * B*H*N entries, the row terms -D_i (D_i = sum_k dO_ik O_ik, stored negated)
+ * and LSE_i * log2(e) (each padded to 256 bytes). Returns 0 for invalid
+ * shapes.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
 
@@ -146,7 +147,8 @@ int fa_bwd(int dtype, const void* q, const void* k, const void* v, const void* o
 /*
  * One of the three launches that make up fa_bwd, for callers that time or
  * schedule them separately. Same arguments and validation as fa_bwd, plus
- *   stage 1: D_i = sum_k dO_ik O_ik and LSE_i * log2(e) into the workspace;
+ *   stage 1: -D_i (D_i = sum_k dO_ik O_ik) and LSE_i * log2(e) into the
+ *            workspace;
  *   stage 2: per block of keys, recompute P and dS tile by tile and write
  *            dK and dV;
  *   stage 3: per block of queries, recompute P and dS tile by tile and
