@@ -103,8 +103,10 @@ int fa_fwd_waves(int dtype, const void* q, const void* k, const void* v, void* o
  * attention). Inputs are OCP FP8 E4M3 codes (1 byte each) with one float32
  * descale per tensor: the real value of Q is q8 * q_descale, and likewise for
  * K and V. S = scale * q_descale * k_descale * (Q8 K8^T) is formed by the fp8
- * MFMA with float32 accumulation; P is scaled by 2^8 and rounded to E4M3 for
- * the P V product; O is written as bfloat16.
+ * MFMA with float32 accumulation; the probabilities, taken against a running
+ * reference max that trails the row max by at most 2^4 (so p <= 2^4), are
+ * scaled by 2^4 and rounded to E4M3 (values <= 256) for the P V product;
+ * O is written as bfloat16.
  *   q8, k8, v8  [B,H,N,d] uint8 E4M3 codes, read only.
  *   o_bf16      [B,H,N,d] bfloat16, written.  lse [B,H,N] float32 or NULL.
  *   d must be 128 for this entry point (FA_ERR_HEADDIM otherwise).

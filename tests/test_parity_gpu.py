@@ -344,6 +344,35 @@ def test_fwd_fp8_small(gpu_lib, N, causal):
     assert lse_rel_err(lse, l_ref) <= 1e-3
 
 
+def _to_e4m3(x):
+    """Per-tensor amax / 448 scaling and a round-to-nearest-even E4M3 cast."""
+    s = float(x.abs().max() / 448.0)
+    return (x / s).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8), s
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("scale", [128 ** -0.5, 0.5])
+def test_fwd_fp8_growing_scores(gpu_lib, causal, scale):
+    """Key norms ramp up along the sequence, so a row's max keeps growing and
+    the running reference max is refreshed many times (by large steps at
+    scale 0.5); O and LSE must still match the oracle on the dequantised
+    inputs."""
+    B, H, N, d = 1, 2, 1500, 128
+    note(f"fwd fp8 ramped keys B{B} H{H} N{N} d{d} scale={scale:.4f} causal={causal}")
+    gen = torch.Generator().manual_seed(6200 + int(causal))
+    q = torch.randn(B, H, N, d, generator=gen)
+    k = torch.randn(B, H, N, d, generator=gen) * torch.linspace(0.05, 2.0, N).view(1, 1, N, 1)
+    v = torch.randn(B, H, N, d, generator=gen)
+    (q8, sq), (k8, sk), (v8, sv) = (_to_e4m3(t) for t in (q, k, v))
+    o, lse = gpu_lib.forward_fp8(*dev(q8, k8, v8), (sq, sk, sv), scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    deq = [oracle.e4m3_decode(t.numpy()) * s for t, s in zip((q8, k8, v8), (sq, sk, sv))]
+    o_ref, l_ref = oracle.attention_forward(*deq, scale, causal)
+    assert np.all(np.isfinite(to64(o)))
+    assert rel_frob(to64(o), o_ref) <= 5e-2
+    assert lse_rel_err(to64(lse), l_ref) <= 1e-3
+
+
 def test_fwd_fp8_workload(gpu_lib):
     B, H, N, d = 2, 32, 8192, 128
     seed = inputs.SEEDS["fp8_8k"]
