@@ -33,6 +33,8 @@ order (fa_fwd_v1: K/V blocks outer, one workgroup per head, O / m / l through
 memory) against the fused forward on the exercise shapes (B=1, H=32, d=128,
 fp16, N = 2048 and 8192, causal and not; and B=8 at N=2048, where the
 first-generation order has one workgroup per CU), one JSON line per case.
+`--fp8 PATH` runs only the fp8 forward on its workload (B2 H32 N8192 d128,
+causal and not), one JSON line per case.
 `--compare-standard PATH` runs only the comparison of the IO-aware forward with
 the standard (materialising) forward that the pages' exercise describes
 (B=1, H=32, d=128, fp16 random normals, N = 2048, 8192, 32768; at least 60 ms
@@ -515,6 +517,45 @@ def run_tile_sweep(path, torch, fa, inputs):
     out.close()
 
 
+def run_fp8(path, torch, fa, inputs, calibrate=False):
+    """The fp8 forward alone on C5's shape (B2 H32 N8192 d128, E4M3 with 1 %
+    x20 outliers), non-causal (the graded case) and causal: medians of 20
+    event-timed launches after at least 60 ms of warm-up, one JSON line each."""
+    if calibrate:
+        src = torch.ones(1 << 28, device="cuda", dtype=torch.float32)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    B, H, N, d = 2, 32, 8192, 128
+    seed = inputs.SEEDS["fp8_8k"]
+    (q8, k8, v8), sc = inputs.draw_fp8(B, H, N, d, seed)
+    q8, k8, v8 = q8.cuda(), k8.cuda(), v8.cuda()
+    o = torch.empty((B, H, N, d), device="cuda", dtype=torch.bfloat16)
+    lse = torch.empty((B, H, N), device="cuda", dtype=torch.float32)
+    out = open(path, "w")
+    for causal in (False, True):
+        fn = lambda: fa.fa_fwd_fp8(q8, k8, v8, sc[0], sc[1], sc[2], o, lse, d ** -0.5, causal)  # noqa
+        warm_up(fn, torch)
+        times = []
+        for _ in range(20):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        med = sorted(times)[len(times) // 2]
+        flops = counted_flops(B, H, N, d, causal)
+        rec = {"workload": f"fwd fp8 e4m3 B{B} H{H} N{N} d{d} causal={causal}", "seed": seed,
+               "median_ms": round(med, 4), "tflops": round(flops / (med * 1e-3) / 1e12, 1),
+               "frac_fp8_peak": round(flops / (med * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)}
+        print(json.dumps(rec), file=out, flush=True)
+        print(f"[fp8] {json.dumps(rec)}", file=sys.stderr, flush=True)
+    out.close()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -535,6 +576,9 @@ def main():
     ap.add_argument("--tile-sweep", metavar="PATH",
                     help="only time the forward's four- and eight-wave workgroup shapes on each "
                          "bf16 forward workload, JSON lines to PATH")
+    ap.add_argument("--fp8", metavar="PATH",
+                    help="only time the fp8 forward on its workload (causal and not), JSON lines "
+                         "to PATH")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device copy, the reference kernel for scaling "
                          "PMC byte counters")
@@ -545,7 +589,7 @@ def main():
               "communication, so the whole-job rate at N GPUs is N times the 1-GPU figure at "
               "the per-GPU head count; run with --gpus 1.", file=sys.stderr, flush=True)
         sys.exit(2)
-    if args.decode or args.compare_standard or args.loop_order or args.tile_sweep:
+    if args.decode or args.compare_standard or args.loop_order or args.tile_sweep or args.fp8:
         import torch
         import exact_io_aware_54_amd as fa
         from exact_io_aware_54_amd import inputs
@@ -560,6 +604,8 @@ def main():
             run_tile_sweep(args.tile_sweep, torch, fa, inputs)
         if args.compare_standard:
             run_compare(args.compare_standard, torch, fa, inputs, args.compare_n)
+        if args.fp8:
+            run_fp8(args.fp8, torch, fa, inputs, args.calibrate_copy)
         return
     run_main(args)
 

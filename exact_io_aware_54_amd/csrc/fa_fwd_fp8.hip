@@ -69,7 +69,7 @@ struct Fp8Wave {
         c = c_;
         const int tid = threadIdx.x;
         lane = tid & 63;
-        wave = tid >> 6;
+        wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar LDS bases
         l32 = lane & 31;
         h = lane >> 5;
         q0 = qb * BM + wave * 32;
