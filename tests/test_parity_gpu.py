@@ -373,6 +373,34 @@ def test_fwd_fp8_growing_scores(gpu_lib, causal, scale):
     assert lse_rel_err(to64(lse), l_ref) <= 1e-3
 
 
+def test_fwd_fp8_max_size(gpu_lib):
+    """The fp8 forward at B*H*N*d just below 2^31 (the ABI's limit): K/V tile
+    offsets and head bases cross 2^30 bytes. E4M3 inputs are quantised on the
+    device from a seeded generator (per-tensor amax / 448, round to nearest
+    even); a first, a middle and the last head are checked against the oracle
+    on the decoded codes, all outputs for finiteness."""
+    B, H, N, d = 511, 32, 1024, 128
+    assert 2 ** 30 + 2 ** 29 < B * H * N * d < 2 ** 31
+    note(f"max size fp8 B{B} H{H} N{N} d{d} non-causal")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(9101)
+    codes, scales = [], []
+    for _ in range(3):
+        x = torch.randn((B, H, N, d), generator=g, device="cuda", dtype=torch.float32)
+        s = float(x.abs().max() / 448.0)
+        codes.append((x / s).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8))
+        scales.append(s)
+        del x
+    o, lse = gpu_lib.forward_fp8(*codes, tuple(scales), scale=d ** -0.5, causal=False)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(lse).all())
+    for b, h in ((0, 0), (B // 2, 17), (B - 1, H - 1)):
+        deq = [oracle.e4m3_decode(c[b, h].cpu().numpy()) * sc for c, sc in zip(codes, scales)]
+        o_ref, l_ref = oracle.attention_forward(*deq, d ** -0.5, False)
+        assert rel_frob(to64(o[b, h]), o_ref) <= 5e-2, (b, h)
+        assert lse_rel_err(to64(lse[b, h]), l_ref) <= 1e-3, (b, h)
+
+
 def test_fwd_fp8_workload(gpu_lib):
     B, H, N, d = 2, 32, 8192, 128
     seed = inputs.SEEDS["fp8_8k"]
