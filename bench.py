@@ -59,7 +59,7 @@ KERNEL_SOURCES = {
     "fwd_mfma_kernel": "exact_io_aware_54_amd/csrc/fa_fwd.hip",
     "bwd_dkdv_kernel": "exact_io_aware_54_amd/csrc/fa_bwd.hip",
     "bwd_dq_kernel": "exact_io_aware_54_amd/csrc/fa_bwd.hip",
-    "fwd_fp8_kernel": "exact_io_aware_54_amd/csrc/fa_fwd_fp8.hip",
+    "fwd_fp8_dma_kernel": "exact_io_aware_54_amd/csrc/fa_fwd_fp8.hip",
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
