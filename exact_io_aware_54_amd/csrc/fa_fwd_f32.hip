@@ -24,8 +24,8 @@ constexpr int F32_NW = 4;   // waves per workgroup, splitting the key tiles
 // running max, sum and output row per query), so a short sequence still
 // keeps four waves busy per query block. At the end the four partial
 // states (m_w, l_w, O_w) of each query are merged exactly as the online
-// softmax merges tiles: m = max m_w, l = sum 2^(m_w - m) l_w (here in natural
-// exponents), O = sum e^(m_w - m) O_w / l.
+// softmax merges tiles: m = max_w m_w, l = sum_w e^(m_w - m) l_w and
+// O = sum_w e^(m_w - m) O_w / l.
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(64 * F32_NW)
 fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
