@@ -35,6 +35,9 @@ fp16, N = 2048 and 8192, causal and not; and B=8 at N=2048, where the
 first-generation order has one workgroup per CU), one JSON line per case.
 `--fp8 PATH` runs only the fp8 forward on its workload (B2 H32 N8192 d128,
 causal and not), one JSON line per case.
+`--bwd-design PATH` times the two-pass backward's launches on the training
+workload against the dQ float atomics a one-pass backward would add
+(fa_probe_dq_atomics), one JSON line per measurement.
 `--compare-standard PATH` runs only the comparison of the IO-aware forward with
 the standard (materialising) forward that the pages' exercise describes
 (B=1, H=32, d=128, fp16 random normals, N = 2048, 8192, 32768; at least 60 ms
@@ -517,6 +520,68 @@ def run_tile_sweep(path, torch, fa, inputs):
     out.close()
 
 
+def _median_ms(fn, torch, n=20):
+    warm_up(fn, torch)
+    times = []
+    for _ in range(n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    return sorted(times)[len(times) // 2]
+
+
+def run_bwd_design(path, torch, fa, inputs):
+    """The backward's structure, measured on the causal B8 H16 N4096 d128
+    workload: the two-pass backward's three launches (row terms, dK/dV, dQ)
+    against the float atomics a one-pass backward would add to its dK/dV pass
+    (fa_probe_dq_atomics: the same stream of dQ partial additions with no
+    arithmetic around it, for 128- and 256-key blocks, and plain stores of the
+    same addresses). Medians of 20 event-timed launches after the warm-up, one
+    JSON line per measurement and a summary line."""
+    B, H, N, d, causal = 8, 16, 4096, 128, True
+    scale = d ** -0.5
+    q, k, v, do = (t.cuda() for t in inputs.draw_qkv(B, H, N, d, inputs.SEEDS["train_4k"],
+                                                      torch.bfloat16, with_do=True))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), device="cuda", dtype=torch.float32)
+    fa.fa_fwd(q, k, v, o, lse, scale, causal)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = fa.workspace_for(q)
+    out = open(path, "w")
+    rec = {"design": "two-pass", "workload": f"bwd bf16 causal B{B} H{H} N{N} d{d}"}
+    for stage, name in ((1, "pre"), (2, "dkdv"), (3, "dq")):
+        fn = lambda s=stage: fa.fa_bwd_stage(s, q, k, v, o, lse, do, dq, dk, dv, ws, scale, causal)  # noqa
+        rec[f"{name}_ms"] = round(_median_ms(fn, torch), 4)
+    rec["bwd_ms"] = round(rec["pre_ms"] + rec["dkdv_ms"] + rec["dq_ms"], 4)
+    print(json.dumps(rec), file=out, flush=True)
+    print(f"[bwd-design] {json.dumps(rec)}", file=sys.stderr, flush=True)
+    acc = torch.zeros(B * H * N * 128, device="cuda", dtype=torch.float32)
+    probes = {}
+    for kb in (128, 256):
+        pairs = sum(N // 64 - (j * kb) // 64 for j in range(N // kb))
+        nbytes = B * H * pairs * 64 * 128 * 4
+        for mode, mname in ((0, "atomic_add"), (1, "plain_store")):
+            fn = lambda kb=kb, m=mode: fa.fa_probe_dq_atomics(acc, B, H, N, kb, m, causal)  # noqa
+            ms = _median_ms(fn, torch)
+            probes[(kb, mname)] = ms
+            r = {"design": "one-pass dQ traffic alone", "key_block": kb, "op": mname,
+                 "median_ms": round(ms, 4), "bytes": nbytes,
+                 "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+            print(json.dumps(r), file=out, flush=True)
+            print(f"[bwd-design] {json.dumps(r)}", file=sys.stderr, flush=True)
+    summ = {"summary": "a one-pass backward takes at least its dQ atomics' time; the two-pass "
+                       "backward's dQ pass is the time it would save",
+            "two_pass_bwd_ms": rec["bwd_ms"], "two_pass_dq_pass_ms": rec["dq_ms"],
+            "one_pass_atomics_ms_kb128": round(probes[(128, "atomic_add")], 4),
+            "one_pass_atomics_ms_kb256": round(probes[(256, "atomic_add")], 4)}
+    print(json.dumps(summ), file=out, flush=True)
+    print(f"[bwd-design] {json.dumps(summ)}", file=sys.stderr, flush=True)
+    out.close()
+
+
 def run_fp8(path, torch, fa, inputs, calibrate=False):
     """The fp8 forward alone on C5's shape (B2 H32 N8192 d128, E4M3 with 1 %
     x20 outliers), non-causal (the graded case) and causal: medians of 20
@@ -579,6 +644,9 @@ def main():
     ap.add_argument("--fp8", metavar="PATH",
                     help="only time the fp8 forward on its workload (causal and not), JSON lines "
                          "to PATH")
+    ap.add_argument("--bwd-design", metavar="PATH",
+                    help="only time the two-pass backward's launches against the dQ float "
+                         "atomics a one-pass backward would add, JSON lines to PATH")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device copy, the reference kernel for scaling "
                          "PMC byte counters")
@@ -589,7 +657,8 @@ def main():
               "communication, so the whole-job rate at N GPUs is N times the 1-GPU figure at "
               "the per-GPU head count; run with --gpus 1.", file=sys.stderr, flush=True)
         sys.exit(2)
-    if args.decode or args.compare_standard or args.loop_order or args.tile_sweep or args.fp8:
+    if (args.decode or args.compare_standard or args.loop_order or args.tile_sweep or args.fp8
+            or args.bwd_design):
         import torch
         import exact_io_aware_54_amd as fa
         from exact_io_aware_54_amd import inputs
@@ -606,6 +675,8 @@ def main():
             run_compare(args.compare_standard, torch, fa, inputs, args.compare_n)
         if args.fp8:
             run_fp8(args.fp8, torch, fa, inputs, args.calibrate_copy)
+        if args.bwd_design:
+            run_bwd_design(args.bwd_design, torch, fa, inputs)
         return
     run_main(args)
 

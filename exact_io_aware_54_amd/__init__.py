@@ -13,7 +13,7 @@ Entry points: ``fa_fwd``, ``fa_fwd_waves``, ``fa_fwd_fp8``, ``fa_bwd``,
 ``fa_bwd_fp8_workspace_bytes``, ``fa_fwd_splitkv``,
 ``fa_fwd_splitkv_workspace_bytes``, ``fa_lse_merge``, ``fa_fwd_v1``,
 ``fa_fwd_v1_workspace_bytes``, ``fa_std_fwd``, ``fa_std_workspace_bytes``,
-``fa_probe_mfma``, ``fa_status_string``, ``fa_version``; ``forward`` / ``backward`` /
+``fa_probe_mfma``, ``fa_probe_dq_atomics``, ``fa_status_string``, ``fa_version``; ``forward`` / ``backward`` /
 ``forward_fp8`` / ``backward_fp8`` / ``forward_splitkv`` / ``forward_v1`` /
 ``forward_standard`` allocate outputs with torch and call them.
 """
@@ -71,6 +71,8 @@ def load_library(path=None):
     lib.fa_fwd_waves.restype = i
     lib.fa_probe_mfma.argtypes = [vp, i, i, vp]
     lib.fa_probe_mfma.restype = i
+    lib.fa_probe_dq_atomics.argtypes = [vp, sz, i, i, i, i, i, i, vp]
+    lib.fa_probe_dq_atomics.restype = i
     lib.fa_bwd_fp8_workspace_bytes.argtypes = [i, i, i, i]
     lib.fa_bwd_fp8_workspace_bytes.restype = sz
     lib.fa_bwd_fp8.argtypes = [vp, vp, vp, f, f, f, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f,
@@ -298,6 +300,16 @@ def fa_probe_mfma(sink, blocks, iters, stream=None):
         raise ValueError("sink must be an int64 device tensor of at least 3*blocks elements")
     _raise("fa_probe_mfma", load_library().fa_probe_mfma(_ptr(sink), int(blocks), int(iters),
                                                           _stream(stream)))
+
+
+def fa_probe_dq_atomics(ws, B, H, N, key_block, mode, causal, stream=None):
+    """Launch the dQ-atomics probe (mode 0 atomics, 1 plain stores); ws is float32 [B*H*N*128]."""
+    import torch
+    if ws.dtype != torch.float32 or not ws.is_cuda or not ws.is_contiguous():
+        raise ValueError("ws must be a contiguous float32 device tensor")
+    _raise("fa_probe_dq_atomics", load_library().fa_probe_dq_atomics(
+        _ptr(ws), ws.numel() * 4, B, H, N, int(key_block), int(mode), int(bool(causal)),
+        _stream(stream)))
 
 
 def fa_fwd_v1_workspace_bytes(B, H, N, d):

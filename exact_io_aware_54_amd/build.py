@@ -1,8 +1,13 @@
 """Build libfa.so (the HIP kernels and the C ABI) in-tree for gfx950 with hipcc.
 
+Each source is compiled to its own object (in parallel, under _build/), then
+the objects are linked into libfa.so. No source calls device code of another,
+so no relocatable device code is needed.
+
 Usage: python -m exact_io_aware_54_amd.build  (or call build()).
 """
 
+import concurrent.futures
 import os
 import subprocess
 import sys
@@ -11,6 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa.so")
+OBJDIR = os.path.join(PKG, "_build")
 
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd_f32.hip", "fa_fwd_fp8.hip", "fa_bwd.hip",
            "fa_std.hip", "fa_splitkv.hip", "fa_v1.hip", "fa_convert.hip", "fa_probe.hip"]
@@ -20,7 +26,6 @@ HIPCC_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-x", "hip",
     # packed fp32 VALU forms are kept out of the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -36,19 +41,37 @@ def hipcc():
     return "hipcc"
 
 
-def build(verbose=False, extra_flags=()):
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc()] + HIPCC_FLAGS + list(extra_flags) + ["-I", os.path.join(ROOT, "include"),
-                                                         "-o", tmp] + srcs
+def _compile(src, obj, extra_flags, verbose):
+    cmd = [hipcc()] + HIPCC_FLAGS + list(extra_flags) + [
+        "-I", os.path.join(ROOT, "include"), "-c", "-o", obj, os.path.join(CSRC, src)]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    return subprocess.run(cmd, capture_output=True, text=True)
+
+
+def build(verbose=False, extra_flags=(), out=LIB, jobs=None):
+    os.makedirs(OBJDIR, exist_ok=True)
+    tag = os.path.splitext(os.path.basename(out))[0]
+    objs = [os.path.join(OBJDIR, f"{tag}.{os.path.splitext(s)[0]}.o") for s in SOURCES]
+    jobs = jobs or min(len(SOURCES), max(1, (os.cpu_count() or 2)))
+    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+        results = list(ex.map(lambda so: _compile(so[0], so[1], extra_flags, verbose),
+                              zip(SOURCES, objs)))
+    failed = [(s, r) for s, r in zip(SOURCES, results) if r.returncode != 0]
+    for s, r in failed:
+        sys.stderr.write(f"--- {s}\n{r.stdout}{r.stderr}")
+    if failed:
+        raise RuntimeError("hipcc failed building libfa.so: " + ", ".join(s for s, _ in failed))
+    tmp = out + ".tmp"
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libfa.so")
-    os.replace(tmp, LIB)
-    return LIB
+        raise RuntimeError("linking libfa.so failed")
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

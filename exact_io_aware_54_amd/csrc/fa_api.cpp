@@ -15,13 +15,25 @@ constexpr int kVersion = 100;  // 0.1.0
 
 // Shape checks shared by the entry points; head dims 64 and 128 everywhere,
 // 256 only where the caller allows it (the 16-bit forward and backward).
+// Every kernel runs a one-dimensional grid of at most 512 work-items per 32
+// rows of each head (B*H*ceil(N/32)*512 in the worst case), and HIP refuses a
+// grid dimension of 2^32 work-items or more: that bounds B*H*ceil(N/32) below
+// 2^23, which matters only for very short sequences (N <= 2 with d = 64
+// would otherwise allow B*H up to 2^25).
 int check_shape(int B, int H, int N, int d, bool allow256 = false) {
     if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
     if (d != 64 && d != 128 && !(allow256 && d == 256)) return FA_ERR_HEADDIM;
     const int64_t total = (int64_t)B * H * N * d;
     if (total >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
+    if ((int64_t)B * H * ((N + 31) / 32) >= ((int64_t)1 << 23)) return FA_ERR_SHAPE;
     return FA_OK;
 }
+
+// Launch failures are read back with hipGetLastError after each launch. An
+// error left pending by earlier, unrelated HIP calls of this host thread
+// would otherwise be reported as this call's: read (and so clear) it once,
+// after validation and before the first launch.
+void clear_pending_error() { (void)hipGetLastError(); }
 
 bool good_scale(float s) { return isfinite(s) && s > 0.f; }
 
@@ -49,6 +61,8 @@ int splitkv_shape(int B, int H, int Nq, int Nk, int d, int num_splits) {
     if (d != 64 && d != 128) return FA_ERR_HEADDIM;
     const int64_t bh = (int64_t)B * H;
     if (bh * Nq * d >= ((int64_t)1 << 31) || bh * Nk * d >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
+    // the merge and split kernels' grids: see check_shape
+    if (bh * ((Nq + 31) / 32) >= ((int64_t)1 << 23)) return FA_ERR_SHAPE;
     if (num_splits < 0 || num_splits > 1024) return FA_ERR_ARG;
     return FA_OK;
 }
@@ -73,7 +87,7 @@ const char* fa_status_string(int status) {
     switch (status) {
         case FA_OK: return "ok";
         case FA_ERR_NULL: return "a required pointer is NULL";
-        case FA_ERR_SHAPE: return "invalid shape (B, H, N must be >= 1 and B*H*N*d < 2^31)";
+        case FA_ERR_SHAPE: return "invalid shape (B, H, N must be >= 1, B*H*N*d < 2^31 and B*H*ceil(N/32) < 2^23)";
         case FA_ERR_DTYPE: return "dtype not supported by this entry point";
         case FA_ERR_HEADDIM: return "head dim not supported";
         case FA_ERR_WORKSPACE: return "workspace too small";
@@ -92,6 +106,7 @@ int fa_fwd(int dtype, const void* q, const void* k, const void* v, void* o, floa
     if (!good_scale(scale)) return FA_ERR_ARG;
     if (!aligned16(q, k, v, o) || !aligned4(lse)) return FA_ERR_ARG;
     const int BH = B * H;
+    clear_pending_error();
     if (dtype == FA_F32)
         return status_of(fa::launch_fwd_f32(d, causal != 0, static_cast<const float*>(q),
                                             static_cast<const float*>(k),
@@ -112,6 +127,7 @@ int fa_fwd_waves(int dtype, const void* q, const void* k, const void* v, void* o
     if (!aligned16(q, k, v, o) || !aligned4(lse)) return FA_ERR_ARG;
     if (waves != 0 && waves != 4 && waves != 8) return FA_ERR_ARG;
     if (d == 256 && waves == 8) return FA_ERR_ARG;
+    clear_pending_error();
     return status_of(fa::launch_fwd_mfma(dtype, d, causal != 0, q, k, v, o, lse, B * H, N, scale,
                                          waves, stream));
 }
@@ -129,6 +145,7 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, float q_descale, 
     const float qk = scale * q_descale * k_descale;
     if (!good_scale(qk)) return FA_ERR_ARG;
     if (!aligned16(q8, k8, v8, o_bf16) || !aligned4(lse)) return FA_ERR_ARG;
+    clear_pending_error();
     return status_of(fa::launch_fwd_fp8(d, causal != 0, q8, k8, v8, qk, v_descale, o_bf16, lse,
                                         B * H, N, stream));
 }
@@ -140,22 +157,34 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
 }
 
 namespace {
-int bwd_common(int dtype, const void* q, const void* k, const void* v, const void* o,
-               const float* lse, const void* dO, void* dq, void* dk, void* dv, void* workspace,
-               size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
-               int stages, hipStream_t stream) {
-    if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
+// Validation shared by the backward entry points (everything but
+// the workspace).
+int bwd_check(int dtype, const void* q, const void* k, const void* v, const void* o,
+              const float* lse, const void* dO, void* dq, void* dk, void* dv, int B, int H, int N,
+              int d, float scale) {
+    if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return FA_ERR_NULL;
     if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
     const int st = check_shape(B, H, N, d, true);
     if (st != FA_OK) return st;
     if (!good_scale(scale)) return FA_ERR_ARG;
     if (!aligned16(q, k, v, o, dO, dq, dk, dv) || !aligned4(lse)) return FA_ERR_ARG;
+    return FA_OK;
+}
+
+int bwd_common(int dtype, const void* q, const void* k, const void* v, const void* o,
+               const float* lse, const void* dO, void* dq, void* dk, void* dv, void* workspace,
+               size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
+               int stages, hipStream_t stream) {
+    const int st = bwd_check(dtype, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale);
+    if (st != FA_OK) return st;
+    if (!workspace) return FA_ERR_NULL;
     if (workspace_bytes < fa_bwd_workspace_bytes(B, H, N, d)) return FA_ERR_WORKSPACE;
     if (((uintptr_t)workspace & 255) != 0) return FA_ERR_WORKSPACE;
     const size_t rows = (size_t)B * H * N;
     float* delta = static_cast<float*>(workspace);
     float* lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                            align256(rows * sizeof(float)));
+    clear_pending_error();
     return status_of(fa::launch_bwd(dtype, d, causal != 0, q, k, v, o, lse, dO, dq, dk, dv,
                                     delta, lse2, B * H, N, scale, stages, stream));
 }
@@ -211,6 +240,7 @@ int fa_bwd_fp8(const void* q8, const void* k8, const void* v8, float q_descale, 
     float* delta = reinterpret_cast<float*>(ws + 3 * align256(el * 2));
     float* lse2 = reinterpret_cast<float*>(ws + 3 * align256(el * 2) + align256(rows * 4));
     hipError_t e;
+    clear_pending_error();
     if ((e = fa::launch_e4m3_to_bf16(q8, qc, el, stream)) != hipSuccess) return FA_ERR_HIP;
     if ((e = fa::launch_e4m3_to_bf16(k8, kc, el, stream)) != hipSuccess) return FA_ERR_HIP;
     if ((e = fa::launch_e4m3_to_bf16(v8, vc, el, stream)) != hipSuccess) return FA_ERR_HIP;
@@ -224,7 +254,25 @@ int fa_probe_mfma(unsigned long long* sink, int blocks, int iters, hipStream_t s
     if (!sink) return FA_ERR_NULL;
     if (blocks < 1 || blocks > 65536 || iters < 1 || iters > (1 << 24)) return FA_ERR_ARG;
     if (((uintptr_t)sink & 7) != 0) return FA_ERR_ARG;
+    clear_pending_error();
     return status_of(fa::launch_mfma_probe(sink, blocks, iters, stream));
+}
+
+int fa_probe_dq_atomics(float* ws, size_t ws_bytes, int B, int H, int N, int key_block,
+                        int mode, int causal, hipStream_t stream) {
+    if (!ws) return FA_ERR_NULL;
+    if (B < 1 || H < 1 || N < 64 || N % 64 != 0) return FA_ERR_SHAPE;
+    if (key_block != 128 && key_block != 256) return FA_ERR_ARG;
+    if (N % key_block != 0) return FA_ERR_SHAPE;
+    if (mode != 0 && mode != 1) return FA_ERR_ARG;
+    const int64_t el = (int64_t)B * H * N * 128;
+    if (el >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
+    if ((int64_t)B * H * (N / key_block) * 512 >= ((int64_t)1 << 32)) return FA_ERR_SHAPE;
+    if (ws_bytes < (size_t)el * sizeof(float)) return FA_ERR_WORKSPACE;
+    if (((uintptr_t)ws & 255) != 0) return FA_ERR_WORKSPACE;
+    clear_pending_error();
+    return status_of(fa::launch_dq_atomic_probe(ws, B * H, N, key_block, mode, causal != 0,
+                                                stream));
 }
 
 size_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits) {
@@ -249,11 +297,13 @@ int fa_fwd_splitkv(int dtype, const void* q, const void* k, const void* v, void*
     if (((uintptr_t)workspace & 255) != 0) return FA_ERR_WORKSPACE;
     const SplitPlan pl = splitkv_plan(B, H, Nq, Nk, num_splits);
     const int BH = B * H;
-    if ((int64_t)BH * ((Nq + 31) / 32) * pl.splits >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
+    // one workgroup of 256 work-items per (batch*head, 32 queries, key range)
+    if ((int64_t)BH * ((Nq + 31) / 32) * pl.splits * 256 >= ((int64_t)1 << 32)) return FA_ERR_SHAPE;
     const size_t rows = (size_t)pl.splits * BH * Nq;
     float* o_part = static_cast<float*>(workspace);
     float* lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                                align256(rows * d * sizeof(float)));
+    clear_pending_error();
     return status_of(fa::launch_fwd_splitkv(dtype, d, causal != 0, q, k, v, o, lse, o_part,
                                             lse_part, BH, Nq, Nk, pl.splits, pl.kps, scale,
                                             stream));
@@ -264,9 +314,11 @@ int fa_lse_merge(int dtype_out, int num_parts, const float* o_parts, const float
     if (!o_parts || !lse_parts || !o) return FA_ERR_NULL;
     if (dtype_out != FA_F32 && dtype_out != FA_F16 && dtype_out != FA_BF16) return FA_ERR_DTYPE;
     if (num_parts < 1 || rows < 1 || d < 4 || d % 4 != 0 || d > 65536) return FA_ERR_SHAPE;
-    if ((int64_t)rows * (d / 4) >= ((int64_t)1 << 38)) return FA_ERR_SHAPE;
+    // one work-item per 4 output elements, in a one-dimensional grid
+    if ((int64_t)rows * (d / 4) > ((int64_t)1 << 32) - 256) return FA_ERR_SHAPE;
     if (!aligned16(o_parts) || !aligned4(lse_parts) || !aligned4(lse)) return FA_ERR_ARG;
     if (((uintptr_t)o & (dtype_out == FA_F32 ? 3 : 1)) != 0) return FA_ERR_ARG;
+    clear_pending_error();
     return status_of(fa::launch_lse_merge(dtype_out, o_parts, lse_parts, num_parts, rows, d, o, lse,
                                           stream));
 }
@@ -294,6 +346,7 @@ int fa_fwd_v1(int dtype, const void* q, const void* k, const void* v, void* o, f
     float* mws = reinterpret_cast<float*>(ws + align256(rows * d * sizeof(float)));
     float* lws = reinterpret_cast<float*>(ws + align256(rows * d * sizeof(float)) +
                                           align256(rows * 2 * sizeof(float)));
+    clear_pending_error();
     return status_of(fa::launch_fwd_v1(dtype, d, causal != 0, q, k, v, o, lse, ows, mws, lws,
                                        B * H, N, scale, stream));
 }
@@ -311,10 +364,14 @@ int fa_std_fwd(int dtype, const void* q, const void* k, const void* v, void* o, 
     const int st = check_shape(B, H, N, d);
     if (st != FA_OK) return st;
     if ((int64_t)B * H > 65535) return FA_ERR_SHAPE;
+    // the score pass has one 256-work-item workgroup per 128 x 128 tile of a head
+    const int64_t ntile = (N + 127) / 128;
+    if (ntile * ntile * 256 >= ((int64_t)1 << 32)) return FA_ERR_SHAPE;
     if (!good_scale(scale)) return FA_ERR_ARG;
     if (!aligned16(q, k, v, o)) return FA_ERR_ARG;
     if (workspace_bytes < fa_std_workspace_bytes(B, H, N, d)) return FA_ERR_WORKSPACE;
     if (((uintptr_t)workspace & 255) != 0) return FA_ERR_WORKSPACE;
+    clear_pending_error();
     return status_of(
         fa::launch_std(dtype, d, causal != 0, q, k, v, o, workspace, B * H, N, scale, stream));
 }

@@ -29,6 +29,8 @@ hipError_t launch_bwd_scaled(int dtype, int d, bool causal, const void* q, const
 hipError_t launch_e4m3_to_bf16(const void* src, void* dst, size_t n, hipStream_t stream);
 hipError_t launch_mfma_probe(unsigned long long* sink, int blocks, int iters,
                              hipStream_t stream);
+hipError_t launch_dq_atomic_probe(float* ws, int BH, int N, int key_block, int mode, int causal,
+                                  hipStream_t stream);
 hipError_t launch_bwd(int dtype, int d, bool causal, const void* q, const void* k, const void* v,
                       const void* o, const float* lse, const void* dO, void* dq, void* dk,
                       void* dv, float* delta, float* lse2, int BH, int N, float scale,

@@ -1,4 +1,6 @@
-// Measurement probe: the practical bf16 MFMA rate and the shader clock.
+// Measurement probes (not part of the attention computation).
+//
+// 1. The practical bf16 MFMA rate and the shader clock.
 //
 // Every wave issues `iters` rounds of four independent 32x32x16 bf16 MFMAs
 // (operands in registers, no memory traffic), so the chip runs at its dense
@@ -45,7 +47,55 @@ mfma_probe_kernel(unsigned long long* __restrict__ sink, int iters) {
     }
 }
 
+// 2. The memory side of a one-pass backward: in that design the dK/dV pass
+// would also form each query block's dQ partial, dS K over its key block, and
+// add it into a float32 dQ accumulator with float atomics, one 64 x 128
+// (d = 128) partial per (key block, 64-query step) pair. This kernel issues
+// exactly that stream of additions with no arithmetic around it: one
+// workgroup of eight waves per (head, block of KB keys), stepping over the
+// 64-query blocks (causal: from the block holding the first key on); wave w
+// adds the 32 x 32 block (query half w / 4, head-dim block w % 4) in the MFMA
+// accumulator layout (16 floats per lane, lanes along the head dim). MODE 0
+// uses float atomic adds (device scope), MODE 1 plain stores of the same
+// addresses (the write bandwidth of the pattern). Its time is a lower bound on
+// what the atomics add to a one-pass dK/dV pass.
+template <int MODE>
+__global__ void __launch_bounds__(512)
+dq_atomic_probe_kernel(float* __restrict__ ws, int N, int nkb, int kb_rows, int causal) {
+    const int bh = blockIdx.x / nkb, kb = blockIdx.x % nkb;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int l32 = lane & 31, h = lane >> 5;
+    const int qsub = wave >> 2, db = wave & 3;
+    float* head = ws + (size_t)bh * N * 128;
+    const int i0 = causal ? (kb * kb_rows) / 64 : 0;
+    float val = 1.0f + 0.001f * (float)lane;
+    for (int ib = i0; ib < N / 64; ++ib) {
+        const int q0 = ib * 64 + 32 * qsub;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float* p = head + (size_t)(q0 + acc_row(r, h)) * 128 + 32 * db + l32;
+            if (MODE == 0)
+                __hip_atomic_fetch_add(p, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else
+                *p = val;
+        }
+        val += 1.0f;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_dq_atomic_probe(float* ws, int BH, int N, int key_block, int mode, int causal,
+                                  hipStream_t stream) {
+    const int nkb = N / key_block;
+    if (mode == 0)
+        hipLaunchKernelGGL(dq_atomic_probe_kernel<0>, dim3(BH * nkb), dim3(512), 0, stream, ws, N,
+                           nkb, key_block, causal);
+    else
+        hipLaunchKernelGGL(dq_atomic_probe_kernel<1>, dim3(BH * nkb), dim3(512), 0, stream, ws, N,
+                           nkb, key_block, causal);
+    return hipGetLastError();
+}
 
 hipError_t launch_mfma_probe(unsigned long long* sink, int blocks, int iters,
                              hipStream_t stream) {

@@ -27,13 +27,22 @@
  *  - Alignment: every [.., N, d] tensor starts on a 16-byte boundary, every
  *    float32 row-statistics array on a 4-byte one (FA_ERR_ARG otherwise).
  *  - d must be 64 or 128 (the 16-bit fa_fwd and fa_bwd also take 256).
- *    B, H, N >= 1 and B*H*N*d < 2^31.
+ *    B, H, N >= 1, B*H*N*d < 2^31 and B*H*ceil(N/32) < 2^23 (the kernels'
+ *    one-dimensional grids stay below 2^32 work-items; the second bound only
+ *    matters for sequences of a few tokens). FA_ERR_SHAPE otherwise.
  *  - causal != 0: query i attends to keys 0..i (the mask is not on the pages;
  *    it is the usual lower-triangular mask with N_q = N_k).
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
  *    and returns without waiting. FA_OK means "launched", not "finished".
- *  - Every argument is validated before anything is launched; on an error
- *    nothing is enqueued and a negative fa_status is returned.
+ *  - Every argument is validated before anything is launched; on a
+ *    validation error (every status except FA_ERR_HIP) nothing is enqueued
+ *    and a negative fa_status is returned.
+ *  - FA_ERR_HIP reports a failure of this call's own launches: an error left
+ *    pending by earlier HIP calls of the same host thread is read and cleared
+ *    before the first launch. Entry points that enqueue several kernels
+ *    (fa_bwd, fa_bwd_fp8, fa_std_fwd, fa_fwd_splitkv) stop at the first
+ *    launch that fails, so the launches before it may already be enqueued;
+ *    their outputs are then undefined.
  *  - Calls are thread-safe; calls that share output buffers on one stream are
  *    ordered by the stream.
  */
@@ -190,7 +199,9 @@ size_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int n
  *              0 to let the library choose about two workgroups per CU.
  *   workspace  at least fa_fwd_splitkv_workspace_bytes(...) bytes, 256-byte
  *              aligned; overwritten.
- * Nq and Nk are any positive sizes with B*H*max(Nq,Nk)*d < 2^31.
+ * Nq and Nk are any positive sizes with B*H*max(Nq,Nk)*d < 2^31 and
+ * B*H*ceil(Nq/32) < 2^23; FA_ERR_SHAPE also if the split grid would reach
+ * 2^32 work-items (B*H*ceil(Nq/32)*splits*256).
  */
 int fa_fwd_splitkv(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
                    int B, int H, int Nq, int Nk, int d, float scale, int causal, int num_splits,
@@ -208,7 +219,8 @@ int fa_fwd_splitkv(int dtype, const void* q, const void* k, const void* v, void*
  *   o_parts    [num_parts][rows][d] float32, 16-byte aligned (FA_ERR_ARG if not).
  *   lse_parts  [num_parts][rows] float32.
  *   o          [rows][d] of dtype_out, written;  lse [rows] float32 or NULL.
- *   d          a multiple of 4 (FA_ERR_SHAPE otherwise).
+ *   d          a multiple of 4 (FA_ERR_SHAPE otherwise); rows * d / 4 at most
+ *              2^32 - 256 (one work-item per four output elements).
  */
 int fa_lse_merge(int dtype_out, int num_parts, const float* o_parts, const float* lse_parts,
                  void* o, float* lse, int rows, int d, hipStream_t stream);
@@ -259,7 +271,8 @@ size_t fa_std_workspace_bytes(int B, int H, int N, int d);
  *   q, k, v, o [B,H,N,d] of `dtype` as in fa_fwd.
  *   workspace  device scratch of at least fa_std_workspace_bytes(B,H,N,d)
  *              bytes, 256-byte aligned; overwritten.
- * Also FA_ERR_SHAPE if B*H > 65535 (grid limit of the score pass).
+ * Also FA_ERR_SHAPE if B*H > 65535 or ceil(N/128)^2 * 256 >= 2^32 (grid limits
+ * of the score pass).
  */
 int fa_std_fwd(int dtype, const void* q, const void* k, const void* v, void* o,
                void* workspace, size_t workspace_bytes,
@@ -309,6 +322,26 @@ int fa_bwd_fp8(const void* q8, const void* k8, const void* v8, float q_descale, 
  *   blocks  1 .. 65536;  iters  1 .. 2^24 (FA_ERR_ARG otherwise).
  */
 int fa_probe_mfma(unsigned long long* sink, int blocks, int iters, hipStream_t stream);
+
+/*
+ * Measurement probe (not part of the attention computation): the memory side
+ * of a one-pass backward, in which the dK/dV pass would also form dQ and add
+ * its per-key-block partials into a float32 accumulator with float atomics
+ * ("11.11 Flash Attention", section "The Recomputation Trade-off": every
+ * (key block, query block) pair contributes to dQ of that query block). For
+ * head dim 128 it issues exactly that stream of additions and nothing else:
+ * one workgroup per (batch*head, block of key_block keys), one 64 x 128 float
+ * partial per 64-query step (causal != 0: steps from the key block's first
+ * query block on), added with device-scope float atomics (mode 0) or written
+ * with plain stores to the same addresses (mode 1). Its duration is a lower
+ * bound on what the atomics would add to such a pass.
+ *   ws         [B*H*N*128] float32 device buffer, 256-byte aligned; its
+ *              contents are accumulated into (mode 0) or overwritten.
+ *   N          a multiple of 64 and of key_block;  key_block 128 or 256.
+ * FA_ERR_SHAPE / FA_ERR_ARG / FA_ERR_WORKSPACE for arguments outside these.
+ */
+int fa_probe_dq_atomics(float* ws, size_t ws_bytes, int B, int H, int N, int key_block,
+                        int mode, int causal, hipStream_t stream);
 
 /* Human-readable text for a fa_status value (static storage, never NULL). */
 const char* fa_status_string(int status);

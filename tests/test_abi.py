@@ -310,3 +310,49 @@ def test_probe_validation(lib):
     assert lib.fa_probe_mfma(FAKE, 4, 0, None) == -7
     assert lib.fa_probe_mfma(FAKE, 65537, 10, None) == -7
     assert lib.fa_probe_mfma(ctypes.c_void_p(0x1004), 4, 10, None) == -7
+
+
+def test_grid_bounds_rejected(lib):
+    """Shapes whose one-dimensional launch grid would reach 2^32 work-items
+    are refused with FA_ERR_SHAPE (HIP would refuse the launch instead)."""
+    # B*H*ceil(N/32) must stay below 2^23: 2^23 heads of one token each
+    assert fwd(lib, B=1 << 12, H=1 << 11, N=1, d=64) == -2
+    assert fwd(lib, B=1 << 12, H=1 << 11, N=1, d=64, dtype=fa.FA_F32) == -2
+    assert fwd(lib, B=1 << 11, H=1 << 11, N=33, d=64) == -2   # 2^22 heads x 2 blocks
+    assert fa.fa_bwd_workspace_bytes(1 << 12, 1 << 11, 1, 64) == 0
+    assert fa.fa_bwd_fp8_workspace_bytes(1 << 12, 1 << 11, 1, 64) == 0
+    assert fa.fa_fwd_v1_workspace_bytes(1 << 12, 1 << 11, 1, 64) == 0
+    # split-KV: 512 heads x 1024 query blocks x 256 key ranges x 256 work-items
+    B, H, Nq, Nk, d = 1, 512, 32768, 32768, 64
+    need = fa.fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, 256)
+    assert need > 0
+    assert lib.fa_fwd_splitkv(fa.FA_BF16, FAKE, FAKE, FAKE, FAKE, None, B, H, Nq, Nk, d, 0.1, 0,
+                              256, ctypes.c_void_p(0x10000), need, None) == -2
+    assert fa.fa_fwd_splitkv_workspace_bytes(1 << 12, 1 << 11, 1, 64, 64, 1) == 0
+    # merge: rows * d / 4 work-items
+    assert lib.fa_lse_merge(fa.FA_F32, 2, ctypes.c_void_p(0x10000), FAKE, FAKE, None, 1 << 30,
+                            64, None) == -2
+    # standard baseline: ceil(N/128)^2 score tiles of 256 work-items
+    N = 1 << 19
+    assert lib.fa_std_fwd(fa.FA_BF16, FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p(0x10000),
+                          fa.fa_std_workspace_bytes(1, 1, N, 64), 1, 1, N, 64, 0.1, 0,
+                          None) == -2
+
+
+def test_probe_dq_atomics_validation(lib):
+    need = 1 * 2 * 256 * 128 * 4
+    ws = ctypes.c_void_p(0x10000)
+
+    def pr(**kw):
+        a = dict(ws=ws, wsb=need, N=256, kb=128, mode=0)
+        a.update(kw)
+        return lib.fa_probe_dq_atomics(a["ws"], a["wsb"], 1, 2, a["N"], a["kb"], a["mode"], 1,
+                                       None)
+
+    assert pr(ws=None) == -1
+    assert pr(N=100) == -2          # not a multiple of 64
+    assert pr(N=320) == -2          # not a multiple of the key block
+    assert pr(kb=64) == -7
+    assert pr(mode=2) == -7
+    assert pr(wsb=need - 4) == -5
+    assert pr(ws=ctypes.c_void_p(0x10010)) == -5

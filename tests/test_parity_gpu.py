@@ -229,6 +229,30 @@ def test_bwd_d256_workload(gpu_lib):
             assert rel_frob(to64(got[b, h]), exp) <= 1e-2, (b, h)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_noncausal_wide_launch(gpu_lib, d):
+    """Non-causal backward on a launch large enough (B*H*ceil(N/256) >= 256)
+    that the dQ pass takes its eight-wave workgroup shape: every element of
+    three whole heads against the oracle."""
+    B, H, N = 4, 16, 2048
+    assert B * H * ((N + 255) // 256) >= 256
+    seed = 4700 + d
+    note(f"bwd bf16 non-causal B{B} H{H} N{N} d{d} seed={seed}")
+    q, k, v, do = inputs.draw_qkv(B, H, N, d, seed, torch.bfloat16, with_do=True)
+    qg, kg, vg, dog = dev(q, k, v, do)
+    o, lse = gpu_lib.forward(qg, kg, vg, causal=False)
+    dq, dk, dv = gpu_lib.backward(qg, kg, vg, o, lse, dog, causal=False)
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv):
+        assert bool(torch.isfinite(t).all())
+    for b, h in ((0, 0), (2, 9), (3, 15)):
+        ref = oracle.attention_backward(to64(q[b, h]), to64(k[b, h]), to64(v[b, h]),
+                                        to64(do[b, h]), d ** -0.5, False)
+        for name, got, exp in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+            assert max_abs(to64(got[b, h]), exp) <= 5e-2, (name, b, h)
+            assert rel_frob(to64(got[b, h]), exp) <= 1e-2, (name, b, h)
+
+
 def test_fwd_bwd_training_workload(gpu_lib):
     """B8 H16 N4096 d128 causal bf16: the shape the benchmark times."""
     B, H, N, d = 8, 16, 4096, 128
@@ -342,6 +366,33 @@ def test_fwd_fp8_small(gpu_lib, N, causal):
     o_ref, l_ref = oracle.attention_forward(q, k, v, 128 ** -0.5, causal)
     assert rel_frob(o, o_ref) <= 5e-2
     assert lse_rel_err(lse, l_ref) <= 1e-3
+
+
+def test_fwd_fp8_score_error(gpu_lib):
+    """Evidence for the fp8 LSE bound. With a single key per head (N = 1) the
+    softmax is trivial: LSE = S = scale * s_q * s_k * sum_d q8 k8 exactly,
+    computed here in float64 from the decoded codes, so the kernel's LSE
+    error is the score error of the fp8 MFMA (plus float32 rounding of the
+    scale product and of exp2/log2 at p = 1). 8192 heads with the C5 recipe
+    (1 % x20 outliers) give scores up to |S| ~ 100. The error measured on
+    MI355X is stated in the assertion below; the fp8 tests' LSE bound,
+    1e-3 * max(1, |LSE|), is that relative score error with headroom."""
+    B, H, N, d = 1, 8192, 1, 128
+    note(f"fp8 score error, one key per head B{B} H{H} N{N} d{d}")
+    (q8, k8, v8), sc = inputs.draw_fp8(B, H, N, d, 6300)
+    o, lse = gpu_lib.forward_fp8(*dev(q8, k8, v8), sc, scale=d ** -0.5, causal=False)
+    torch.cuda.synchronize()
+    q = oracle.e4m3_decode(q8.numpy()) * sc[0]
+    k = oracle.e4m3_decode(k8.numpy()) * sc[1]
+    s_ref = (q * k).sum(-1)[..., 0] * d ** -0.5            # [B, H]: one score per head
+    err = np.abs(to64(lse)[..., 0] - s_ref)
+    rel = err / np.maximum(1.0, np.abs(s_ref))
+    print(f"[fp8 score error] max |S| {np.abs(s_ref).max():.1f}, max abs err {err.max():.3e}, "
+          f"max err / max(1,|S|) {rel.max():.3e}, median {np.median(rel):.3e}", flush=True)
+    assert rel.max() <= 1e-3
+    # O of a single key is that key's V row (P = 1 exactly)
+    v = oracle.e4m3_decode(v8.numpy()) * sc[2]
+    assert rel_frob(to64(o), v) <= 5e-3
 
 
 def _to_e4m3(x):
