@@ -9,7 +9,8 @@ in the library's kernels; there is no fallback path. If the library has not
 been built, calls raise ``RuntimeError``.
 
 Entry points: ``fa_fwd``, ``fa_fwd_waves``, ``fa_fwd_fp8``, ``fa_bwd``,
-``fa_bwd_stage``, ``fa_bwd_workspace_bytes``, ``fa_bwd_fp8``,
+``fa_bwd_stage``, ``fa_bwd_workspace_bytes``, ``fa_bwd_noalloc``,
+``fa_bwd_noalloc_max_rows``, ``fa_bwd_fp8``,
 ``fa_bwd_fp8_workspace_bytes``, ``fa_fwd_splitkv``,
 ``fa_fwd_splitkv_workspace_bytes``, ``fa_lse_merge``, ``fa_fwd_v1``,
 ``fa_fwd_v1_workspace_bytes``, ``fa_std_fwd``, ``fa_std_workspace_bytes``,
@@ -29,6 +30,7 @@ FA_OK = 0
 STATUS = {
     0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_DTYPE",
     -4: "FA_ERR_HEADDIM", -5: "FA_ERR_WORKSPACE", -6: "FA_ERR_HIP", -7: "FA_ERR_ARG",
+    -8: "FA_ERR_TOO_LARGE",
 }
 
 _lib = None
@@ -61,6 +63,10 @@ def load_library(path=None):
     lib.fa_bwd.restype = i
     lib.fa_bwd_stage.argtypes = [i] + lib.fa_bwd.argtypes
     lib.fa_bwd_stage.restype = i
+    lib.fa_bwd_noalloc.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+    lib.fa_bwd_noalloc.restype = i
+    lib.fa_bwd_noalloc_max_rows.argtypes = []
+    lib.fa_bwd_noalloc_max_rows.restype = sz
     lib.fa_fwd_splitkv_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.fa_fwd_splitkv_workspace_bytes.restype = sz
     lib.fa_fwd_splitkv.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
@@ -220,6 +226,27 @@ def fa_bwd_stage(stage, q, k, v, o, lse, do, dq, dk, dv, workspace, scale, causa
                           workspace.numel(), B, H, N, d, float(scale), int(bool(causal)),
                           _stream(stream))
     _raise("fa_bwd_stage", st)
+
+
+def fa_bwd_noalloc(q, k, v, o, lse, do, dq, dk, dv, scale, causal, stream=None):
+    """fa_bwd without a workspace: the row terms live in the library's own
+    per-device scratch (for callers that cannot allocate). Calls that overlap
+    in time on one device race on that scratch."""
+    import torch
+    lib = load_library()
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do), ("dq", dq),
+                    ("dk", dk), ("dv", dv)):
+        _check_bhnd(name, t, (B, H, N, d), q.dtype)
+    _check_bhnd("lse", lse, (B, H, N), torch.float32)
+    st = lib.fa_bwd_noalloc(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                            _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, float(scale),
+                            int(bool(causal)), _stream(stream))
+    _raise("fa_bwd_noalloc", st)
+
+
+def fa_bwd_noalloc_max_rows():
+    return int(load_library().fa_bwd_noalloc_max_rows())
 
 
 def fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, num_splits=0):

@@ -19,7 +19,8 @@ LIB = os.path.join(PKG, "libfa.so")
 OBJDIR = os.path.join(PKG, "_build")
 
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd_f32.hip", "fa_fwd_fp8.hip", "fa_bwd.hip",
-           "fa_std.hip", "fa_splitkv.hip", "fa_v1.hip", "fa_convert.hip", "fa_probe.hip"]
+           "fa_std.hip", "fa_splitkv.hip", "fa_v1.hip", "fa_convert.hip", "fa_probe.hip",
+           "fa_noalloc.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

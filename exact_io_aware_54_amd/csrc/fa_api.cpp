@@ -93,6 +93,7 @@ const char* fa_status_string(int status) {
         case FA_ERR_WORKSPACE: return "workspace too small";
         case FA_ERR_HIP: return "HIP runtime error at launch";
         case FA_ERR_ARG: return "invalid scalar argument (scale, descale, split count) or misaligned pointer";
+        case FA_ERR_TOO_LARGE: return "problem larger than the library's fixed scratch (fa_bwd_noalloc: B*H*N above fa_bwd_noalloc_max_rows())";
         default: return "unknown status";
     }
 }
@@ -206,6 +207,30 @@ int fa_bwd_stage(int stage, int dtype, const void* q, const void* k, const void*
     return bwd_common(dtype, q, k, v, o, lse, dO, dq, dk, dv, workspace, workspace_bytes, B, H, N,
                       d, scale, causal, 1 << (stage - 1), stream);
 }
+
+int fa_bwd_noalloc(int dtype, const void* q, const void* k, const void* v, const void* o,
+                   const float* lse, const void* dO, void* dq, void* dk, void* dv, int B, int H,
+                   int N, int d, float scale, int causal, hipStream_t stream) {
+    const int st = bwd_check(dtype, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, scale);
+    if (st != FA_OK) return st;
+    if ((size_t)B * H * N > fa::kNoallocMaxRows) return FA_ERR_TOO_LARGE;
+    // the scratch is per device: the current one, which must own the stream
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_HIP;
+    if (stream != nullptr) {
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return FA_ERR_HIP;
+        if (sdev != dev) return FA_ERR_ARG;
+    }
+    float* delta = nullptr;
+    float* lse2 = nullptr;
+    if (fa::noalloc_scratch(dev, &delta, &lse2) != hipSuccess) return FA_ERR_HIP;
+    clear_pending_error();
+    return status_of(fa::launch_bwd(dtype, d, causal != 0, q, k, v, o, lse, dO, dq, dk, dv,
+                                    delta, lse2, B * H, N, scale, 7, stream));
+}
+
+size_t fa_bwd_noalloc_max_rows(void) { return fa::kNoallocMaxRows; }
 
 size_t fa_bwd_fp8_workspace_bytes(int B, int H, int N, int d) {
     if (check_shape(B, H, N, d, true) != FA_OK) return 0;

@@ -44,6 +44,12 @@ hipError_t launch_lse_merge(int dtype_out, const float* o_parts, const float* ls
 hipError_t launch_fwd_v1(int dtype, int d, bool causal, const void* q, const void* k,
                          const void* v, void* o, float* lse, float* ows, float* mws, float* lws,
                          int BH, int N, float scale, hipStream_t stream);
+// Scratch of fa_bwd_noalloc: room for the row terms of this many rows
+// (B*H*N), two float vectors, 16 MiB per device in all.
+constexpr size_t kNoallocMaxRows = (size_t)1 << 21;
+// This device's copy of that scratch (`device` must be the current device):
+// -D at *delta, LSE * log2 e at *lse2, kNoallocMaxRows floats each.
+hipError_t noalloc_scratch(int device, float** delta, float** lse2);
 hipError_t launch_std(int dtype, int d, bool causal, const void* q, const void* k, const void* v,
                       void* o, void* s, int BH, int N, float scale, hipStream_t stream);
 

@@ -70,9 +70,11 @@ typedef enum {
     FA_ERR_HEADDIM = -4,    /* d not supported by this entry point               */
     FA_ERR_WORKSPACE = -5,  /* workspace too small or not 256-byte aligned      */
     FA_ERR_HIP = -6,        /* the HIP runtime reported an error at launch       */
-    FA_ERR_ARG = -7         /* a scalar argument is invalid (scale not finite or
+    FA_ERR_ARG = -7,        /* a scalar argument is invalid (scale not finite or
                                not positive, descale not finite or <= 0, split
                                count out of range) or a pointer is misaligned    */
+    FA_ERR_TOO_LARGE = -8   /* the problem does not fit the library's fixed
+                               scratch (fa_bwd_noalloc only)                    */
 } fa_status;
 
 /*
@@ -172,6 +174,33 @@ int fa_bwd_stage(int stage, int dtype, const void* q, const void* k, const void*
                  const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv,
                  void* workspace, size_t workspace_bytes,
                  int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/*
+ * fa_bwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. Same
+ * computation, kernels and results (bit for bit) as fa_bwd; the row terms
+ * that fa_bwd keeps in the caller's workspace live instead in a scratch
+ * array inside the library, one per GPU, 16 MiB, allocated with the library's
+ * code object and held until the process ends. Nothing is allocated or freed
+ * by the call, and no memset is enqueued (every scratch entry a call reads
+ * is first written by that call's own first kernel, so no clearing is
+ * needed).
+ *   Arguments as fa_bwd, without the workspace. The stream must belong to
+ *   the current device (FA_ERR_ARG otherwise); NULL is that device's default
+ *   stream.
+ *   B*H*N must not exceed fa_bwd_noalloc_max_rows() (2^21): FA_ERR_TOO_LARGE
+ *   otherwise, checked before anything is launched.
+ * The scratch is shared by every call on one GPU and keeps the last call's
+ * contents: calls that overlap in time on one GPU (different streams, or
+ * different host threads) race on it and give wrong gradients. Serialise
+ * them, e.g. on one stream.
+ */
+int fa_bwd_noalloc(int dtype, const void* q, const void* k, const void* v, const void* o,
+                   const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                   int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/* The largest B*H*N that fa_bwd_noalloc accepts (2^21). */
+size_t fa_bwd_noalloc_max_rows(void);
 
 /*
  * Size in bytes of the scratch buffer fa_fwd_splitkv needs for these

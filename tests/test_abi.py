@@ -339,6 +339,29 @@ def test_grid_bounds_rejected(lib):
                           None) == -2
 
 
+def test_bwd_noalloc_validation(lib):
+    """fa_bwd_noalloc validates like fa_bwd and refuses problems beyond its
+    fixed scratch before any HIP call."""
+    assert fa.fa_bwd_noalloc_max_rows() == 1 << 21
+
+    def nb(**kw):
+        a = dict(dtype=fa.FA_BF16, q=FAKE, dq=FAKE, B=1, H=2, N=64, d=64, scale=0.1)
+        a.update(kw)
+        return lib.fa_bwd_noalloc(a["dtype"], a["q"], FAKE, FAKE, FAKE, FAKE, FAKE, a["dq"], FAKE,
+                                  FAKE, a["B"], a["H"], a["N"], a["d"], a["scale"], 1, None)
+
+    assert nb(q=None) == -1
+    assert nb(dq=None) == -1
+    assert nb(dtype=fa.FA_F32) == -3
+    assert nb(d=96) == -4
+    assert nb(B=0) == -2
+    assert nb(scale=0.0) == -7
+    assert nb(dq=ctypes.c_void_p(0x1008)) == -7
+    assert nb(B=32, H=64, N=1025) == -8           # one row more than 2^21 (= 32*64*1024)
+    assert nb(B=1, H=1, N=(1 << 21) + 1) == -8
+    assert fa.fa_status_string(-8) != "unknown status"
+
+
 def test_probe_dq_atomics_validation(lib):
     need = 1 * 2 * 256 * 128 * 4
     ws = ctypes.c_void_p(0x10000)
