@@ -16,9 +16,9 @@ Frobenius error ||gpu - oracle|| / ||oracle||):
   fp32 probabilities, so LSE carries only fp32-level error (~1e-5); 1e-3
   leaves room for exp2/log2 approximations at N = 16K.
   LSE of the fp8 path: |error| <= 1e-3 * max(1, |LSE|). With the x20 outliers
-  the scores reach |S| ~ 170, and the fp8 MFMA's internal accumulation was
-  measured to carry a relative error of ~2e-4 of |S| (absolute 0.03 at
-  S = 170), so the bound scales with the magnitude.
+  the scores reach |S| ~ 150, and the fp8 MFMA's score error alone reaches
+  6.8e-4 of |S| (test_fwd_fp8_score_error: one key per head, where LSE = S
+  exactly), so the bound scales with the magnitude.
 Full-size workloads compare every element of sampled heads, or sampled query
 rows computed one by one by the oracle (each output row depends only on its
 own query row); properties that hold at any size are checked on all heads.
@@ -373,10 +373,13 @@ def test_fwd_fp8_score_error(gpu_lib):
     softmax is trivial: LSE = S = scale * s_q * s_k * sum_d q8 k8 exactly,
     computed here in float64 from the decoded codes, so the kernel's LSE
     error is the score error of the fp8 MFMA (plus float32 rounding of the
-    scale product and of exp2/log2 at p = 1). 8192 heads with the C5 recipe
-    (1 % x20 outliers) give scores up to |S| ~ 100. The error measured on
-    MI355X is stated in the assertion below; the fp8 tests' LSE bound,
-    1e-3 * max(1, |LSE|), is that relative score error with headroom."""
+    scale product and of exp2/log2 at p = 1). 8192 heads with the fp8
+    workload's recipe (1 % x20 outliers) give scores up to |S| ~ 150.
+    Measured on MI355X: max |error| / max(1, |S|) = 6.8e-4 (0.022 at
+    |S| = 153), median 1.4e-5 -- far above float32 accumulation of 128 exact
+    products (~1e-6), so the fp8 MFMA's internal sums are coarser than fp32.
+    The fp8 tests' LSE bound, 1e-3 * max(1, |LSE|), is that score error with
+    ~1.5x headroom; this test holds it to the same bound."""
     B, H, N, d = 1, 8192, 1, 128
     note(f"fp8 score error, one key per head B{B} H{H} N{N} d{d}")
     (q8, k8, v8), sc = inputs.draw_fp8(B, H, N, d, 6300)

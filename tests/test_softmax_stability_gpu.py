@@ -10,8 +10,13 @@
 Tolerances are the 16-bit ones: O max-abs <= 2e-2 and relative Frobenius <=
 1e-2, LSE max-abs <= 1e-3 (|LSE| reaches ~40 here and the scores are exact
 products of the rounded inputs accumulated in fp32), dQ/dK/dV relative
-Frobenius <= 1e-2 and max-abs <= 5e-2 * max(1, max|ref|) (gradients reach
-tens here; the bfloat16 rounding of dS and of the outputs is relative)."""
+Frobenius <= 1e-2 and max-abs <= 5e-2 * max(1, max|ref|).
+The gradient max-abs bar is deliberately looser than the plain 5e-2 of the
+parity tests: at scale 1 the gradients reach tens, where the bfloat16
+rounding of dS and of the stored gradients alone is 2^-9 of the magnitude
+(~0.06 at 30), so an absolute 5e-2 would fail any 16-bit kernel; scaling by
+the largest reference magnitude keeps the bar at 5e-2 for unit-scale
+gradients, and the relative Frobenius bar is unchanged."""
 
 import numpy as np
 import pytest
