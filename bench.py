@@ -292,6 +292,10 @@ def run_suite(path, torch, fa, inputs):
          "train_4k"),
         ("bwd bf16 causal B1 H32 N8192 d256", "bwd", torch.bfloat16, 1, 32, 8192, 256, True,
          "causal_8k"),
+        ("fwd bf16 B1 H32 N8192 d256 (non-causal)", "fwd", torch.bfloat16, 1, 32, 8192, 256,
+         False, "causal_8k"),
+        ("bwd bf16 B1 H32 N8192 d256 (non-causal)", "bwd", torch.bfloat16, 1, 32, 8192, 256,
+         False, "causal_8k"),
         ("fwd fp8 B2 H32 N8192 d128", "fp8", None, 2, 32, 8192, 128, False, "fp8_8k"),
         ("fwd f32 B1 H2 N128 d64", "fwd", torch.float32, 1, 2, 128, 64, False, "tiny_f32"),
     ]
