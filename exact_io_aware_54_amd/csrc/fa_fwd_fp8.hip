@@ -7,11 +7,11 @@
 //  * S^T = K8 Q8^T runs on the gfx950 32x32x64 f8f6f4 MFMA (E4M3 x E4M3,
 //    fp32 accumulate). The per-tensor descales and the softmax scale fold
 //    into one factor c = scale * q_descale * k_descale * log2(e).
-//  * O^T = V8^T P8^T is one 32x32x64 MFMA per 64-key tile and 32 head dims;
+//  * O^T = V8^T P8^T is one 32x32x64 MFMA per 64 keys and 32 head dims;
 //    the epilogue multiplies by v_descale / l and writes bf16.
 //
 // gfx950 mapping:
-//  * K and V tiles (64 keys x 128 bytes) go HBM -> LDS with global_load_lds
+//  * K and V tiles (64 or 128 keys x 128 bytes) go HBM -> LDS with global_load_lds
 //    into row-major tiles whose 16-byte chunks are XOR-swizzled
 //    (tile_swz<64>: rows of 128 bytes), double-buffered, no VGPR staging.
 //  * K is read as two 16-byte chunks per MFMA operand (32 bytes of a key row).
@@ -35,17 +35,22 @@ namespace fa {
 namespace {
 
 constexpr int F8_D = 128;       // head dim (bytes per K / V row)
-constexpr int F8_BN = 64;        // keys per tile
 constexpr float F8_GROW = 4.f;   // log2 units: refresh the reference max when it grows by > 2^4
 
 // Four waves of 32 queries per workgroup, two workgroups per CU (measured
-// faster than eight-wave workgroups on the C5 shape, causal and not).
+// faster than eight-wave workgroups on the B2 H32 N8192 shape, causal and
+// not). Tiles of 128 keys without the causal mask (half the per-tile fixed
+// work -- barrier, cross-lane max, refresh test -- per key: 6 % faster on that
+// shape), 64 with it (3 % faster there: less work wasted on the diagonal).
 template <bool CAUSAL>
 struct Fp8Wave {
+    static constexpr int F8_BN = CAUSAL ? 64 : 128;  // keys per tile
+    static constexpr int F8_NSUB = F8_BN / 32;       // 32-key score subtiles per tile
+    static constexpr int F8_NK = F8_BN / 64;         // 64-key P V products per head-dim block
     static constexpr int NW = 4;
     static constexpr int BM = 32 * NW;
     static constexpr int NT = 64 * NW;
-    static constexpr int TILEB = F8_BN * F8_D;          // 8 KiB
+    static constexpr int TILEB = F8_BN * F8_D;       // 8 or 16 KiB
     static constexpr int NLOAD = TILEB / (NT * 16);
     static_assert(NLOAD >= 1 && TILEB % (NT * 16) == 0, "whole direct loads");
 
@@ -140,13 +145,13 @@ struct Fp8Wave {
         if (kt + 1 < nkt) issue_tile((kt + 1) * F8_BN, kn, vn);
         const int kbase = kt * F8_BN;
         if (CAUSAL && kbase > q0 + 31) return;
-        f32x16 s[2];
-        s[0] = f32x16{};
-        s[1] = f32x16{};
+        f32x16 s[F8_NSUB];
+#pragma unroll
+        for (int c2 = 0; c2 < F8_NSUB; ++c2) s[c2] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2) {
+            for (int c2 = 0; c2 < F8_NSUB; ++c2) {
                 const i32x4 lo = *reinterpret_cast<const i32x4*>(kb + koff[ks][0] + c2 * 32 * F8_D);
                 const i32x4 hi = *reinterpret_cast<const i32x4*>(kb + koff[ks][1] + c2 * 32 * F8_D);
                 const i32x8 a{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -156,7 +161,7 @@ struct Fp8Wave {
         if (need_mask) {
             const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - kbase - 4 * h;
 #pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2)
+            for (int c2 = 0; c2 < F8_NSUB; ++c2)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     if (32 * c2 + 8 * (r >> 2) + (r & 3) > lim) s[c2][r] = -INFINITY;
@@ -165,7 +170,9 @@ struct Fp8Wave {
 #pragma unroll
         for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+        for (int c2 = 1; c2 < F8_NSUB; ++c2)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[c2][r]);
         mx = wave_half_max(mx) * c;
         if (__builtin_amdgcn_ballot_w64(mx > m_run + F8_GROW) != 0) {
             const float m_new = fmaxf(m_run, mx);
@@ -179,9 +186,9 @@ struct Fp8Wave {
         }
         const float moff = F8_GROW - m_run;   // p * 2^4 = 2^(s c - m + 4)
         float rs = 0.f;
-        i32x8 pf;
+        i32x8 pf[F8_NK];
 #pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2)
+        for (int c2 = 0; c2 < F8_NSUB; ++c2)
 #pragma unroll
             for (int r = 0; r < 16; r += 4) {
                 float p[4];
@@ -193,20 +200,22 @@ struct Fp8Wave {
                 int w = 0;
                 w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], w, false);
                 w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
-                pf[4 * c2 + r / 4] = w;
+                pf[c2 / 2][4 * (c2 % 2) + r / 4] = w;
             }
         l_run += rs;
         typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            i32x2 t[4];
+        for (int kc = 0; kc < F8_NK; ++kc)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                t[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                    (lds_i32x2*)(vb + voff[b] + (16 * (r & 1) + 32 * (r >> 1)) * F8_D));
-            const i32x8 a{t[0][0], t[0][1], t[1][0], t[1][1], t[2][0], t[2][1], t[3][0], t[3][1]};
-            oacc[b] = mfma32_fp8(a, pf, oacc[b]);
-        }
+            for (int b = 0; b < 4; ++b) {
+                i32x2 t[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    t[r] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                        (lds_i32x2*)(vb + voff[b] + (64 * kc + 16 * (r & 1) + 32 * (r >> 1)) * F8_D));
+                const i32x8 a{t[0][0], t[0][1], t[1][0], t[1][1], t[2][0], t[2][1], t[3][0], t[3][1]};
+                oacc[b] = mfma32_fp8(a, pf[kc], oacc[b]);
+            }
     }
 
     __device__ __forceinline__ void finish(__bf16* Oh, float* lse_h, float out_scale) {
