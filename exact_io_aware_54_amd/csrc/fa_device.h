@@ -83,20 +83,22 @@ __device__ __forceinline__ int xcd_remap(int id, int G) {
 // blocks first and all XCDs should get the same total work. Block ids go to
 // the eight XCDs in turn.
 //  - BH a multiple of 8: xcd_remap hands every XCD BH/8 whole heads; within
-//    an XCD the heads go in groups of G (4, 2 or 1, dividing BH/8), each
-//    group's query blocks longest first with its heads taken in turn. Taking the long
-//    blocks of a few heads before the short ones leaves no long block for
-//    the end of the launch, while the running blocks of an XCD still read
-//    the K/V of only a few heads.
+//    an XCD the heads go in groups of G (at most gmax: 4, 2 or 1, dividing
+//    BH/8), each group's query blocks longest first with its heads taken in
+//    turn. Taking the long blocks of a few heads before the short ones leaves
+//    no long block for the end of the launch, while the running blocks of an
+//    XCD still read the K/V of only a few heads (fewer heads: fewer bytes
+//    fetched past the XCD's L2, more imbalance at the end).
 //  - otherwise the XCD ranges would split heads and one XCD would get the
 //    long half of a head: the blocks are dealt instead, longest first over
 //    all heads, block id k being the k-th longest, so XCD x gets every
 //    eighth one.
-__device__ __forceinline__ void causal_block(int id, int nqb, int BH, int& bh, int& qb) {
+__device__ __forceinline__ void causal_block(int id, int nqb, int BH, int& bh, int& qb,
+                                             int gmax = 4) {
     if ((BH & 7) == 0) {
         const int L = xcd_remap(id, BH * nqb);
         const int hx = BH >> 3;  // heads per XCD
-        const int G = (hx & 3) == 0 ? 4 : (hx & 1) == 0 ? 2 : 1;
+        const int G = ((hx & 3) == 0 && gmax >= 4) ? 4 : ((hx & 1) == 0 && gmax >= 2) ? 2 : 1;
         const int grp = L / (G * nqb), j = L - grp * G * nqb;
         bh = grp * G + j % G;
         qb = nqb - 1 - j / G;
