@@ -85,3 +85,52 @@ def test_noalloc_at_the_limit(gpu_lib):
         fa.fa_bwd_noalloc(q2, q2, q2, q2, l2, q2, q2, q2, q2, d ** -0.5, True)
     assert exc.value.status == -8
     assert np.isfinite(to64(got[0][0, 0, :64])).all()
+
+
+def test_noalloc_graph_capture(gpu_lib):
+    """The callers it is for: forward + fa_bwd_noalloc captured into a HIP
+    graph (through torch's capture) and replayed four times, with eager work
+    between the replays that includes a different-size fa_bwd_noalloc call
+    (which leaves its own contents in the shared scratch); every replay must
+    give the eager result bit for bit."""
+    fa = gpu_lib
+    B, H, N, d = 2, 4, 1000, 128
+    note(f"noalloc under graph capture: bf16 causal B{B} H{H} N{N} d{d}")
+    q, k, v, do = (t.cuda() for t in inputs.draw_qkv(B, H, N, d, 7106, torch.bfloat16,
+                                                        with_do=True))
+    scale = d ** -0.5
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), device="cuda", dtype=torch.float32)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+
+    def step():
+        fa.fa_fwd(q, k, v, o, lse, scale, True)
+        fa.fa_bwd_noalloc(q, k, v, o, lse, do, dq, dk, dv, scale, True)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (o, lse, dq, dk, dv)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm-up on the capture stream
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    # a different problem between replays, through the same scratch
+    q2, k2, v2, do2 = (t.cuda() for t in inputs.draw_qkv(1, 3, 777, 64, 7107, torch.bfloat16,
+                                                            with_do=True))
+    o2, l2 = fa.forward(q2, k2, v2, causal=False)
+    g2 = tuple(torch.empty_like(q2) for _ in range(3))
+    for rep in range(4):
+        for t in (o, lse, dq, dk, dv):
+            t.fill_(float("nan"))
+        fa.fa_bwd_noalloc(q2, k2, v2, o2, l2, do2, *g2, 64 ** -0.5, False)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, exp in zip((o, lse, dq, dk, dv), ref):
+            assert torch.equal(got, exp), rep
