@@ -35,6 +35,12 @@
 #include "fa_device.h"
 #include "fa_launch.h"
 
+// Head dim 256 runs one wave per SIMD: no partner wave covers the LDS
+// latency, so its operand reads run kPf256 MFMA units ahead (B1 H32 N8192:
+// dQ -9 %, causal dK/dV -7 %, non-causal dK/dV -1 % against the compiler's own
+// order; one ahead was slower than the compiler's order)
+constexpr int kPf256 = 4;
+
 namespace fa {
 namespace {
 
@@ -564,15 +570,23 @@ struct Dkdv1Wave {
                 for (int i = 0; i < 4; ++i) pacc[4 * r4 + i] = nd[i];
             }
         }
+        // one wave per SIMD: the Q (and dO) row operands are read PF k-steps
+        // ahead of their MFMAs, order kept by scheduling fences
+        constexpr int PF = kPf256;
+        V8 oq[PF], og[PF];
+        auto rows = [&](int s, V8& aq, V8& ag) {
+            const int ro = tile_off<D>(l32, 16 * s + 8 * h);
+            aq = *reinterpret_cast<const V8*>(sQ + ro);
+            if (DK) ag = *reinterpret_cast<const V8*>(sG + ro);
+        };
+#pragma unroll
+        for (int s = 0; s < PF; ++s) rows(s, oq[s], og[s]);
 #pragma unroll
         for (int s = 0; s < C::KS; ++s) {
-            const int ro = tile_off<D>(l32, 16 * s + 8 * h);
-            const V8 aq = *reinterpret_cast<const V8*>(sQ + ro);
-            sacc = mfma32(aq, kf[s], sacc);
-            if (DK) {
-                const V8 ag = *reinterpret_cast<const V8*>(sG + ro);
-                pacc = mfma32(ag, vf[DK ? s : 0], pacc);
-            }
+            sacc = mfma32(oq[s % PF], kf[s], sacc);
+            if (DK) pacc = mfma32(og[s % PF], vf[DK ? s : 0], pacc);
+            if (s + PF < C::KS) rows(s + PF, oq[s % PF], og[s % PF]);
+            __builtin_amdgcn_sched_barrier(0);
         }
         // causal: a wave-uniform branch, so only diagonal and ragged-edge steps
         // pay for the mask; non-causal keeps one path (a second one makes the
@@ -594,14 +608,21 @@ struct Dkdv1Wave {
         const char* src = DK ? sQ : sG;
         const int src_r = 4 * h + (lane & 15) / 4;
         const int src_d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        auto tr = [&](int u) {  // unit u: g2 = u / DB, b = u % DB
+            const int g2 = u / C::DB, b = u % C::DB;
+            return tr_read8<V8>(src, tile_off<D>(16 * g2 + src_r, 32 * b + src_d),
+                                tile_off<D>(16 * g2 + 8 + src_r, 32 * b + src_d));
+        };
+        constexpr int NC = 2 * C::DB;
+        V8 ta[PF];
 #pragma unroll
-        for (int g2 = 0; g2 < 2; ++g2)
+        for (int u = 0; u < PF; ++u) ta[u] = tr(u);
 #pragma unroll
-            for (int b = 0; b < C::DB; ++b) {
-                const V8 a = tr_read8<V8>(src, tile_off<D>(16 * g2 + src_r, 32 * b + src_d),
-                                          tile_off<D>(16 * g2 + 8 + src_r, 32 * b + src_d));
-                acc[b] = mfma32(a, op[g2], acc[b]);
-            }
+        for (int u = 0; u < NC; ++u) {
+            acc[u % C::DB] = mfma32(ta[u % PF], op[u / C::DB], acc[u % C::DB]);
+            if (u + PF < NC) ta[u % PF] = tr(u + PF);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
 
     __device__ __forceinline__ void finish(T* outh, float mul) const {
@@ -793,7 +814,7 @@ struct DqWave {
         // k-step t / 2, subtile t % 2), order kept by scheduling fences; one
         // ahead with the fences measured 1-2 % faster than the compiler's own
         // order, two ahead spills in the eight-wave causal shape
-        constexpr int NU = 2 * C::KS, PF = 1;
+        constexpr int NU = 2 * C::KS, PF = D > 128 ? kPf256 : 1;
         V8 ok[PF], ov[PF];
         auto kv_unit = [&](int t, V8& ak, V8& av) {
             const int o = roff[t >> 1] + (t & 1) * 32 * C::ROWB;
@@ -833,7 +854,7 @@ struct DqWave {
         sf[3] = pack8<T>(dp[1], 8);
         // dQ^T += K^T dS^T (unit u: key group g = u / DB, b = u % DB), the
         // transposed K operands read PT units ahead
-        constexpr int NC = 4 * C::DB, PT = 1;
+        constexpr int NC = 4 * C::DB, PT = D > 128 ? kPf256 : 1;
         V8 ta[PT];
 #pragma unroll
         for (int u = 0; u < PT; ++u)
@@ -863,12 +884,22 @@ struct DqWave {
         for (int c2 = 0; c2 < 2; ++c2) {
             if (CAUSAL && kbase + 32 * c2 > q0 + 31) break;  // the half lies past every query
             f32x16 s = f32x16{}, dp = dinit;
+            constexpr int PF = kPf256;  // operand reads PF k-steps ahead
+            V8 ok[PF], ov[PF];
+#pragma unroll
+            for (int ks = 0; ks < PF; ++ks) {
+                ok[ks] = *reinterpret_cast<const V8*>(kb + roff[ks] + c2 * 32 * C::ROWB);
+                ov[ks] = *reinterpret_cast<const V8*>(vb + roff[ks] + c2 * 32 * C::ROWB);
+            }
 #pragma unroll
             for (int ks = 0; ks < C::KS; ++ks) {
-                const V8 ak = *reinterpret_cast<const V8*>(kb + roff[ks] + c2 * 32 * C::ROWB);
-                const V8 av = *reinterpret_cast<const V8*>(vb + roff[ks] + c2 * 32 * C::ROWB);
-                s = mfma32(ak, qf[ks], s);
-                dp = mfma32(av, gf[ks], dp);
+                s = mfma32(ok[ks % PF], qf[ks], s);
+                dp = mfma32(ov[ks % PF], gf[ks], dp);
+                if (ks + PF < C::KS) {
+                    ok[ks % PF] = *reinterpret_cast<const V8*>(kb + roff[ks + PF] + c2 * 32 * C::ROWB);
+                    ov[ks % PF] = *reinterpret_cast<const V8*>(vb + roff[ks + PF] + c2 * 32 * C::ROWB);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
             if (need_mask) {
 #pragma unroll
@@ -881,14 +912,19 @@ struct DqWave {
                 dp[r] = SEED ? p * dp[r] : p * (dp[r] + del);  // dP - D; del holds -D
             }
             const V8 sf0 = pack8<T>(dp, 0), sf1 = pack8<T>(dp, 8);
+            auto tr = [&](int u) {  // unit u: g = u / DB, b = u % DB
+                return tr_read8<V8>(kb + (2 * c2 + u / C::DB) * 16 * C::ROWB,
+                                    toff[0][u % C::DB], toff[1][u % C::DB]);
+            };
+            V8 ta[PF];
 #pragma unroll
-            for (int g = 0; g < 2; ++g)
+            for (int u = 0; u < PF; ++u) ta[u] = tr(u);
 #pragma unroll
-                for (int b = 0; b < C::DB; ++b) {
-                    const V8 a = tr_read8<V8>(kb + (2 * c2 + g) * 16 * C::ROWB, toff[0][b],
-                                              toff[1][b]);
-                    dqacc[b] = mfma32(a, g == 0 ? sf0 : sf1, dqacc[b]);
-                }
+            for (int u = 0; u < 2 * C::DB; ++u) {
+                dqacc[u % C::DB] = mfma32(ta[u % PF], u < C::DB ? sf0 : sf1, dqacc[u % C::DB]);
+                if (u + PF < 2 * C::DB) ta[u % PF] = tr(u + PF);
+                __builtin_amdgcn_sched_barrier(0);
+            }
             __builtin_amdgcn_sched_barrier(0);  // keep the halves apart
         }
     }
