@@ -14,16 +14,21 @@ Entry points: ``fa_fwd``, ``fa_fwd_waves``, ``fa_fwd_fp8``, ``fa_bwd``,
 ``fa_bwd_fp8_workspace_bytes``, ``fa_fwd_splitkv``,
 ``fa_fwd_splitkv_workspace_bytes``, ``fa_lse_merge``, ``fa_fwd_v1``,
 ``fa_fwd_v1_workspace_bytes``, ``fa_std_fwd``, ``fa_std_workspace_bytes``,
-``fa_probe_mfma``, ``fa_probe_dq_atomics``, ``fa_status_string``, ``fa_version``; ``forward`` / ``backward`` /
+``fa_probe_mfma``, ``fa_probe_dq_atomics``, ``fa_status_string``,
+``fa_version``, ``fa_build_flags``; ``forward`` / ``backward`` /
 ``forward_fp8`` / ``backward_fp8`` / ``forward_splitkv`` / ``forward_v1`` /
 ``forward_standard`` allocate outputs with torch and call them.
+``library_override(SERIAL_LIB_PATH)`` routes the wrappers through the
+race-guard build for the duration of a ``with`` block.
 """
 
+import contextlib
 import ctypes
 import os
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
+SERIAL_LIB_PATH = os.path.join(PKG_DIR, "libfa_serial.so")
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 FA_OK = 0
@@ -96,8 +101,23 @@ def load_library(path=None):
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
     lib.fa_version.restype = i
+    lib.fa_build_flags.argtypes = []
+    lib.fa_build_flags.restype = i
     _lib = lib
     return lib
+
+
+@contextlib.contextmanager
+def library_override(path):
+    """Route every wrapper through another build of the library (such as the
+    race-guard build libfa_serial.so) inside the block, then restore."""
+    global _lib
+    saved = _lib
+    _lib = None
+    try:
+        yield load_library(path)
+    finally:
+        _lib = saved
 
 
 def fa_status_string(status):
@@ -106,6 +126,10 @@ def fa_status_string(status):
 
 def fa_version():
     return load_library().fa_version()
+
+
+def fa_build_flags():
+    return load_library().fa_build_flags()
 
 
 # ------------------------------------------------------------------ marshalling

@@ -4,7 +4,12 @@ Each source is compiled to its own object (in parallel, under _build/), then
 the objects are linked into libfa.so. No source calls device code of another,
 so no relocatable device code is needed.
 
-Usage: python -m exact_io_aware_54_amd.build  (or call build()).
+build_all() also links libfa_serial.so, the race-guard build: the same sources
+with FA_SERIAL_STAGING defined, so that every double-buffered kernel loads its
+next LDS tile only after the current one is consumed. Its outputs must match
+libfa.so bit for bit; it is a test build, not a product path.
+
+Usage: python -m exact_io_aware_54_amd.build  (or call build_all()).
 """
 
 import concurrent.futures
@@ -16,6 +21,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa.so")
+LIB_SERIAL = os.path.join(PKG, "libfa_serial.so")
 OBJDIR = os.path.join(PKG, "_build")
 
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd_f32.hip", "fa_fwd_fp8.hip", "fa_bwd.hip",
@@ -75,5 +81,12 @@ def build(verbose=False, extra_flags=(), out=LIB, jobs=None):
     return out
 
 
+def build_all(verbose=False, jobs=None):
+    """libfa.so, then the race-guard build libfa_serial.so."""
+    return [build(verbose=verbose, jobs=jobs),
+            build(verbose=verbose, extra_flags=("-DFA_SERIAL_STAGING",), out=LIB_SERIAL,
+                  jobs=jobs)]
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print("\n".join(build_all(verbose=True)))

@@ -83,6 +83,14 @@ extern "C" {
 
 int fa_version(void) { return kVersion; }
 
+int fa_build_flags(void) {
+#ifdef FA_SERIAL_STAGING
+    return FA_BUILD_SERIAL_STAGING;
+#else
+    return 0;
+#endif
+}
+
 const char* fa_status_string(int status) {
     switch (status) {
         case FA_OK: return "ok";

@@ -249,7 +249,7 @@ struct DkdvWave {
         const int qbase = ib * C::BM;
         __builtin_amdgcn_s_waitcnt(kVmcntZero);
         __syncthreads();
-        if (ib + 1 < nqb) issue(qbase + C::BM, nQ, nG, nL, nD);
+        if (!kSerialStaging && ib + 1 < nqb) issue(qbase + C::BM, nQ, nG, nL, nD);
         const int qb0 = qbase + 32 * qs;  // first query of this wave's subtile
         if (CAUSAL && key0 > qb0 + 31) return;  // every query of the subtile precedes every key
 
@@ -418,9 +418,18 @@ bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     const int i0 = CAUSAL ? (kb * C::BN) / C::BM : 0;
     w.issue_kv(K + head, V + head, kb * C::BN, sK, sV);
     w.issue(i0 * C::BM, sQ0, sG0, sL0, sD0);
-    for (int ib = i0; ib < nqb; ib += 2) {
-        w.step(ib, nqb, sK, sV, sQ0, sG0, sL0, sD0, sQ1, sG1, sL1, sD1);
-        if (ib + 1 < nqb) w.step(ib + 1, nqb, sK, sV, sQ1, sG1, sL1, sD1, sQ0, sG0, sL0, sD0);
+    if constexpr (kSerialStaging) {
+        for (int ib = i0; ib < nqb; ++ib) {
+            w.step(ib, nqb, sK, sV, sQ0, sG0, sL0, sD0, sQ0, sG0, sL0, sD0);
+            __syncthreads();
+            if (ib + 1 < nqb) w.issue((ib + 1) * C::BM, sQ0, sG0, sL0, sD0);
+        }
+    } else {
+        for (int ib = i0; ib < nqb; ib += 2) {
+            w.step(ib, nqb, sK, sV, sQ0, sG0, sL0, sD0, sQ1, sG1, sL1, sD1);
+            if (ib + 1 < nqb)
+                w.step(ib + 1, nqb, sK, sV, sQ1, sG1, sL1, sD1, sQ0, sG0, sL0, sD0);
+        }
     }
     // sum the two query halves: subtile-1 waves park their partials in LDS
     __syncthreads();
@@ -556,7 +565,7 @@ struct Dkdv1Wave {
         const int qbase = ib * C::BM;
         __builtin_amdgcn_s_waitcnt(kVmcntZero);
         __syncthreads();
-        if (ib + 1 < nqb) issue(qbase + C::BM, nQ, nG, nL, nD);
+        if (!kSerialStaging && ib + 1 < nqb) issue(qbase + C::BM, nQ, nG, nL, nD);
         if (CAUSAL && key0 > qbase + C::BM - 1) return;  // every query of the block precedes every key
 
         // S = Q K^T (and dP - D = dO V^T - D, the dP accumulators starting from
@@ -673,9 +682,17 @@ bwd_dkdv1_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __re
     const int nqb = (N + C::BM - 1) / C::BM;
     const int i0 = CAUSAL ? (kb * C::BN) / C::BM : 0;
     w.issue(i0 * C::BM, sQ0, sG0, sL0, sD0);
-    for (int ib = i0; ib < nqb; ib += 2) {
-        w.step(ib, nqb, sQ0, sG0, sL0, sD0, sQ1, sG1, sL1, sD1);
-        if (ib + 1 < nqb) w.step(ib + 1, nqb, sQ1, sG1, sL1, sD1, sQ0, sG0, sL0, sD0);
+    if constexpr (kSerialStaging) {
+        for (int ib = i0; ib < nqb; ++ib) {
+            w.step(ib, nqb, sQ0, sG0, sL0, sD0, sQ0, sG0, sL0, sD0);
+            __syncthreads();
+            if (ib + 1 < nqb) w.issue((ib + 1) * C::BM, sQ0, sG0, sL0, sD0);
+        }
+    } else {
+        for (int ib = i0; ib < nqb; ib += 2) {
+            w.step(ib, nqb, sQ0, sG0, sL0, sD0, sQ1, sG1, sL1, sD1);
+            if (ib + 1 < nqb) w.step(ib + 1, nqb, sQ1, sG1, sL1, sD1, sQ0, sG0, sL0, sD0);
+        }
     }
     w.finish(out + head, DK ? scale : 1.f);
 }
@@ -797,7 +814,7 @@ struct DqWave {
         const int kbase = kt * C::BN;
         __builtin_amdgcn_s_waitcnt(kVmcntZero);
         __syncthreads();
-        if (kt + 1 < nkt) issue(kbase + C::BN, kn, vn);
+        if (!kSerialStaging && kt + 1 < nkt) issue(kbase + C::BN, kn, vn);
         if (CAUSAL && kbase > q0 + 31) return;
         if constexpr (D > 128 && !CAUSAL) {
             step_halves(kbase, kb, vb);
@@ -970,9 +987,17 @@ bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __restr
     DqWave<T, D, CAUSAL, NW> w;
     w.init(Q + head, K + head, V + head, dO + head, lse2 + rowbase, delta + rowbase, N, qb, c);
     w.issue(0, sK0, sV0);
-    for (int kt = 0; kt < w.nkt; kt += 2) {
-        w.step(kt, sK0, sV0, sK1, sV1);
-        if (kt + 1 < w.nkt) w.step(kt + 1, sK1, sV1, sK0, sV0);
+    if constexpr (kSerialStaging) {
+        for (int kt = 0; kt < w.nkt; ++kt) {
+            w.step(kt, sK0, sV0, sK0, sV0);
+            __syncthreads();
+            if (kt + 1 < w.nkt) w.issue((kt + 1) * C::BN, sK0, sV0);
+        }
+    } else {
+        for (int kt = 0; kt < w.nkt; kt += 2) {
+            w.step(kt, sK0, sV0, sK1, sV1);
+            if (kt + 1 < w.nkt) w.step(kt + 1, sK1, sV1, sK0, sV0);
+        }
     }
     w.finish(dQ + head, scale);
 }

@@ -152,4 +152,19 @@ __device__ __forceinline__ int tile_off(int r, int d) {
 
 constexpr int kVmcntZero = 0x0F70;  // s_waitcnt vmcnt(0), expcnt/lgkmcnt untouched
 
+// The streamed tiles (K/V in the forward passes and the dQ pass, Q/dO/LSE/D
+// in the dK/dV pass) are double-buffered: the direct-to-LDS loads of tile i+1
+// go into the second buffer set while tile i is computed on. A missing wait or
+// barrier there would let a wave read a tile that is still landing, or let the
+// next load overwrite one that a slower wave still reads. The race-guard build
+// (FA_SERIAL_STAGING defined) keeps one buffer set and loads each tile only
+// after every wave is done with the previous one and waits for it before any
+// read: no overlap, so no race, and the same arithmetic in the same order. Its
+// outputs must equal the product build's bit for bit.
+#ifdef FA_SERIAL_STAGING
+constexpr bool kSerialStaging = true;
+#else
+constexpr bool kSerialStaging = false;
+#endif
+
 }  // namespace fa

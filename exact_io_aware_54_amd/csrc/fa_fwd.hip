@@ -176,7 +176,7 @@ struct FwdWave {
         // barrier for everyone's), and the other buffers are no longer read
         __builtin_amdgcn_s_waitcnt(kVmcntZero);
         __syncthreads();
-        if (kt + 1 < nkt) issue_tile(kbase + C::BN, kn, vn);
+        if (!kSerialStaging && kt + 1 < nkt) issue_tile(kbase + C::BN, kn, vn);
 
         const bool active = !CAUSAL || kbase <= q0 + 31;
         if (!active) return;
@@ -326,9 +326,17 @@ fwd_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __res
     FwdWave<T, D, CAUSAL, NW> w;
     w.init(Q + head, K + head, V + head, N, qb, c);
     w.issue_tile(0, sK0, sV0);
-    for (int kt = 0; kt < w.nkt; kt += 2) {
-        w.step(kt, sK0, sV0, sK1, sV1);
-        if (kt + 1 < w.nkt) w.step(kt + 1, sK1, sV1, sK0, sV0);
+    if constexpr (kSerialStaging) {
+        for (int kt = 0; kt < w.nkt; ++kt) {
+            w.step(kt, sK0, sV0, sK0, sV0);
+            __syncthreads();
+            if (kt + 1 < w.nkt) w.issue_tile((kt + 1) * C::BN, sK0, sV0);
+        }
+    } else {
+        for (int kt = 0; kt < w.nkt; kt += 2) {
+            w.step(kt, sK0, sV0, sK1, sV1);
+            if (kt + 1 < w.nkt) w.step(kt + 1, sK1, sV1, sK0, sV0);
+        }
     }
     w.finish(O + head, LSE == nullptr ? nullptr : LSE + (size_t)bh * N);
 }

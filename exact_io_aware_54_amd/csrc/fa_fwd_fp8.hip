@@ -142,7 +142,7 @@ struct Fp8Wave {
                                          uint8_t* vn) {
         __builtin_amdgcn_s_waitcnt(kVmcntZero);
         __syncthreads();
-        if (kt + 1 < nkt) issue_tile((kt + 1) * F8_BN, kn, vn);
+        if (!kSerialStaging && kt + 1 < nkt) issue_tile((kt + 1) * F8_BN, kn, vn);
         const int kbase = kt * F8_BN;
         if (CAUSAL && kbase > q0 + 31) return;
         f32x16 s[F8_NSUB];
@@ -258,9 +258,17 @@ fwd_fp8_dma_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
     W w;
     w.init(Q + head, K + head, V + head, N, qb, c);
     w.issue_tile(0, sK0, sV0);
-    for (int kt = 0; kt < w.nkt; kt += 2) {
-        w.step(kt, sK0, sV0, sK1, sV1);
-        if (kt + 1 < w.nkt) w.step(kt + 1, sK1, sV1, sK0, sV0);
+    if constexpr (kSerialStaging) {
+        for (int kt = 0; kt < w.nkt; ++kt) {
+            w.step(kt, sK0, sV0, sK0, sV0);
+            __syncthreads();
+            if (kt + 1 < w.nkt) w.issue_tile((kt + 1) * W::F8_BN, sK0, sV0);
+        }
+    } else {
+        for (int kt = 0; kt < w.nkt; kt += 2) {
+            w.step(kt, sK0, sV0, sK1, sV1);
+            if (kt + 1 < w.nkt) w.step(kt + 1, sK1, sV1, sK0, sV0);
+        }
     }
     w.finish(O + head, LSE == nullptr ? nullptr : LSE + (size_t)bh * N, out_scale);
 }

@@ -277,16 +277,26 @@ splitkv_kernel(const T* __restrict__ Q, const T* __restrict__ K, const T* __rest
     const int kstop = CAUSAL ? min(kend, min(qb * C::BQ + C::BQ, Nq) - 1 + (Nk - Nq) + 1) : kend;
     const int nkt = kstop > kbeg ? (kstop - kbeg + C::BN - 1) / C::BN : 0;
     if (nkt > 0) w.issue(kbeg, sK0, sV0);
-    for (int kt = 0; kt < nkt; kt += 2) {
-        __builtin_amdgcn_s_waitcnt(kVmcntZero);
-        __syncthreads();
-        if (kt + 1 < nkt) w.issue(kbeg + (kt + 1) * C::BN, sK1, sV1);
-        w.step(kbeg + kt * C::BN, sK0, sV0);
-        if (kt + 1 < nkt) {
+    if constexpr (kSerialStaging) {
+        for (int kt = 0; kt < nkt; ++kt) {
             __builtin_amdgcn_s_waitcnt(kVmcntZero);
             __syncthreads();
-            if (kt + 2 < nkt) w.issue(kbeg + (kt + 2) * C::BN, sK0, sV0);
-            w.step(kbeg + (kt + 1) * C::BN, sK1, sV1);
+            w.step(kbeg + kt * C::BN, sK0, sV0);
+            __syncthreads();
+            if (kt + 1 < nkt) w.issue(kbeg + (kt + 1) * C::BN, sK0, sV0);
+        }
+    } else {
+        for (int kt = 0; kt < nkt; kt += 2) {
+            __builtin_amdgcn_s_waitcnt(kVmcntZero);
+            __syncthreads();
+            if (kt + 1 < nkt) w.issue(kbeg + (kt + 1) * C::BN, sK1, sV1);
+            w.step(kbeg + kt * C::BN, sK0, sV0);
+            if (kt + 1 < nkt) {
+                __builtin_amdgcn_s_waitcnt(kVmcntZero);
+                __syncthreads();
+                if (kt + 2 < nkt) w.issue(kbeg + (kt + 2) * C::BN, sK0, sV0);
+                w.step(kbeg + (kt + 1) * C::BN, sK1, sV1);
+            }
         }
     }
     __syncthreads();  // the tile buffers are reused for the merge

@@ -388,16 +388,26 @@ std_pv_kernel(const T* __restrict__ P, const T* __restrict__ V, T* __restrict__ 
     w.init(P, V, N, bh, qb);
     const int nkt = (N + C::BN - 1) / C::BN;
     w.issue(0, sV0, sP0);
-    for (int kt = 0; kt < nkt; kt += 2) {
-        __builtin_amdgcn_s_waitcnt(kVmcntZero);
-        __syncthreads();
-        if (kt + 1 < nkt) w.issue((kt + 1) * C::BN, sV1, sP1);
-        w.tile(kt * C::BN, sV0, sP0);
-        if (kt + 1 < nkt) {
+    if constexpr (kSerialStaging) {
+        for (int kt = 0; kt < nkt; ++kt) {
             __builtin_amdgcn_s_waitcnt(kVmcntZero);
             __syncthreads();
-            if (kt + 2 < nkt) w.issue((kt + 2) * C::BN, sV0, sP0);
-            w.tile((kt + 1) * C::BN, sV1, sP1);
+            w.tile(kt * C::BN, sV0, sP0);
+            __syncthreads();
+            if (kt + 1 < nkt) w.issue((kt + 1) * C::BN, sV0, sP0);
+        }
+    } else {
+        for (int kt = 0; kt < nkt; kt += 2) {
+            __builtin_amdgcn_s_waitcnt(kVmcntZero);
+            __syncthreads();
+            if (kt + 1 < nkt) w.issue((kt + 1) * C::BN, sV1, sP1);
+            w.tile(kt * C::BN, sV0, sP0);
+            if (kt + 1 < nkt) {
+                __builtin_amdgcn_s_waitcnt(kVmcntZero);
+                __syncthreads();
+                if (kt + 2 < nkt) w.issue((kt + 2) * C::BN, sV0, sP0);
+                w.tile((kt + 1) * C::BN, sV1, sP1);
+            }
         }
     }
     w.finish(O, bh);

@@ -378,6 +378,17 @@ const char* fa_status_string(int status);
 /* Library ABI version: major * 10000 + minor * 100 + patch. */
 int fa_version(void);
 
+/* Build variant flags. FA_BUILD_SERIAL_STAGING is set in the race-guard build
+ * (libfa_serial.so), where every kernel that double-buffers its streamed K/V
+ * (or Q/dO) tiles in LDS instead keeps one buffer and loads the next tile only
+ * once the current one is consumed, so no load overlaps a read. Same
+ * arithmetic, same order: its outputs must equal the product build's bit for
+ * bit, which tests that the product build's waits and barriers are complete.
+ * The guard concerns the tiles that page 2 ("11.11 Flash Attention", section
+ * "The Tiling Algorithm") streams through on-chip memory. 0 in libfa.so. */
+#define FA_BUILD_SERIAL_STAGING 1
+int fa_build_flags(void);
+
 #ifdef __cplusplus
 }
 #endif

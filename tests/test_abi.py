@@ -157,9 +157,32 @@ def test_library_has_no_unresolved_kernel_stubs():
     # A kernel whose host-side launch stub was not emitted shows up as an
     # undefined __device_stub__ symbol and makes dlopen fail on first use.
     import subprocess
-    out = subprocess.run(["nm", "-D", fa.LIB_PATH], capture_output=True, text=True).stdout
-    missing = [ln for ln in out.splitlines() if " U " in ln and "__device_stub__" in ln]
-    assert missing == []
+    for path in (fa.LIB_PATH, fa.SERIAL_LIB_PATH):
+        if not os.path.exists(path):
+            continue
+        out = subprocess.run(["nm", "-D", path], capture_output=True, text=True).stdout
+        missing = [ln for ln in out.splitlines() if " U " in ln and "__device_stub__" in ln]
+        assert missing == [], path
+
+
+def test_race_guard_build_flags(lib):
+    # The product library reports no build variant; the race-guard build
+    # (serial LDS staging) loads, exports the same symbols and says what it is.
+    assert fa.fa_build_flags() == 0
+    if not os.path.exists(fa.SERIAL_LIB_PATH):
+        from exact_io_aware_54_amd import build
+        build.build_all()
+    serial = ctypes.CDLL(fa.SERIAL_LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(serial, n), n
+    serial.fa_build_flags.restype = ctypes.c_int
+    assert serial.fa_build_flags() == 1
+    with fa.library_override(fa.SERIAL_LIB_PATH):
+        assert fa.fa_build_flags() == 1
+        # validation is shared: an invalid call is rejected the same way
+        assert fa.load_library().fa_fwd(2, None, FAKE, FAKE, FAKE, None, 1, 1, 64, 64,
+                                        0.125, 0, None) == -1
+    assert fa.fa_build_flags() == 0
 
 
 def test_splitkv_workspace_bytes(lib):

@@ -1,0 +1,151 @@
+"""Race guard: the product library against its serial-staging build, bit for bit.
+
+Every kernel that streams tiles through LDS (K/V in the forward passes, the
+split-KV forward, the standard baseline's P V pass and the dQ pass; Q/dO with
+their LSE and D rows in the dK/dV passes) double-buffers them: the loads of
+tile i+1 land in the second buffer set while tile i is computed on, and only
+a wait for the wave's own loads plus a workgroup barrier separate a tile's
+arrival from its first read and its last read from its next overwrite. The
+race-guard build libfa_serial.so (FA_SERIAL_STAGING) keeps one buffer set and
+loads tile i+1 only after a barrier that follows every read of tile i, then
+waits for it before any read, so nothing can race there; the arithmetic and
+its order are unchanged. A wait or barrier missing from the product build
+shows up as a difference here (at shapes with many tiles, ragged tails, both
+workgroup shapes and every head dim), so the two builds must agree exactly.
+"""
+
+import os
+
+import pytest
+import torch
+
+from exact_io_aware_54_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def note(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def serial(gpu_lib):
+    path = gpu_lib.SERIAL_LIB_PATH
+    if not os.path.exists(path):
+        pytest.fail(f"race-guard build missing at {path}; build it with "
+                    "`python -m exact_io_aware_54_amd.build`")
+    assert gpu_lib.fa_build_flags() == 0
+    with gpu_lib.library_override(path):
+        assert gpu_lib.fa_build_flags() == 1
+    return path
+
+
+def both(fa, serial, fn):
+    """fn() through libfa.so, then through libfa_serial.so."""
+    a = fn()
+    torch.cuda.synchronize()
+    with fa.library_override(serial):
+        b = fn()
+        torch.cuda.synchronize()
+    return a, b
+
+
+def assert_same(a, b):
+    for x, y in zip(a, b):
+        assert x.dtype == y.dtype and x.shape == y.shape
+        assert torch.equal(x, y), (x.float() - y.float()).abs().max().item()
+
+
+def fwd_waves(fa, q, k, v, causal, waves):
+    B, H, N, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32)
+    fa.fa_fwd_waves(q, k, v, o, lse, d ** -0.5, causal, waves)
+    return o, lse
+
+
+@pytest.mark.parametrize("d,waves", [(64, 4), (64, 8), (128, 4), (128, 8), (256, 4)])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1000, 2113])
+def test_forward(gpu_lib, serial, d, waves, causal, N):
+    note(f"race guard fwd bf16 B1 H3 N{N} d{d} waves={waves} causal={causal}")
+    q, k, v = (t.cuda() for t in inputs.draw_qkv(1, 3, N, d, 9100 + N + d, torch.bfloat16))
+    a, b = both(gpu_lib, serial, lambda: fwd_waves(gpu_lib, q, k, v, causal, waves))
+    assert_same(a, b)
+
+
+def test_forward_f16_headline_shape(gpu_lib, serial):
+    note("race guard fwd f16 B2 H16 N4096 d128 causal")
+    q, k, v = (t.cuda() for t in inputs.draw_qkv(2, 16, 4096, 128, 9200, torch.float16))
+    a, b = both(gpu_lib, serial, lambda: gpu_lib.forward(q, k, v, causal=True))
+    assert_same(a, b)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1000, 4096])
+def test_forward_fp8(gpu_lib, serial, causal, N):
+    note(f"race guard fwd fp8 B1 H4 N{N} d128 causal={causal}")
+    (q8, k8, v8), sc = inputs.draw_fp8(1, 4, N, 128, 9300 + N)
+    q8, k8, v8 = q8.cuda(), k8.cuda(), v8.cuda()
+    a, b = both(gpu_lib, serial, lambda: gpu_lib.forward_fp8(q8, k8, v8, sc, causal=causal))
+    assert_same(a, b)
+
+
+def backward_case(fa, B, H, N, d, causal, seed):
+    q, k, v, do = (t.cuda() for t in inputs.draw_qkv(B, H, N, d, seed, torch.bfloat16,
+                                                     with_do=True))
+    o, lse = fa.forward(q, k, v, causal=causal)
+    return lambda: fa.backward(q, k, v, o, lse, do, causal=causal)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward(gpu_lib, serial, d, causal):
+    # B1 H3: four-wave dQ pass; the dK/dV pass is the eight-wave one at
+    # d <= 128 and the split dV / dK launches at d = 256
+    note(f"race guard bwd bf16 B1 H3 N1000 d{d} causal={causal}")
+    fn = backward_case(gpu_lib, 1, 3, 1000, d, causal, 9400 + d)
+    a, b = both(gpu_lib, serial, fn)
+    assert_same(a, b)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_wide(gpu_lib, serial, d, causal):
+    # B1 H64 N1056: B*H*ceil(N/256) >= 256 selects the eight-wave dQ pass
+    note(f"race guard bwd bf16 B1 H64 N1056 d{d} causal={causal}")
+    fn = backward_case(gpu_lib, 1, 64, 1056, d, causal, 9500 + d)
+    a, b = both(gpu_lib, serial, fn)
+    assert_same(a, b)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_fp8(gpu_lib, serial, causal):
+    note(f"race guard bwd fp8 B1 H2 N700 d128 causal={causal}")
+    (q8, k8, v8), sc = inputs.draw_fp8(1, 2, 700, 128, 9600)
+    q8, k8, v8 = q8.cuda(), k8.cuda(), v8.cuda()
+    g = torch.Generator().manual_seed(9601)
+    do = torch.randn((1, 2, 700, 128), generator=g).to(torch.bfloat16).cuda()
+    o, lse = gpu_lib.forward_fp8(q8, k8, v8, sc, causal=causal)
+    a, b = both(gpu_lib, serial,
+                lambda: gpu_lib.backward_fp8(q8, k8, v8, sc, o, lse, do, causal=causal))
+    assert_same(a, b)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq,nk,splits", [(1, 5000, 0), (16, 5000, 7), (300, 1300, 3)])
+def test_splitkv(gpu_lib, serial, causal, nq, nk, splits):
+    note(f"race guard splitkv bf16 B2 H4 Nq{nq} Nk{nk} d128 splits={splits} causal={causal}")
+    q, k, v = (t.cuda() for t in inputs.draw_qkv_rect(2, 4, nq, nk, 128, 9700 + nq,
+                                                      torch.bfloat16))
+    a, b = both(gpu_lib, serial,
+                lambda: gpu_lib.forward_splitkv(q, k, v, causal=causal, num_splits=splits))
+    assert_same(a, b)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_standard(gpu_lib, serial, causal):
+    note(f"race guard standard bf16 B1 H2 N1000 d128 causal={causal}")
+    q, k, v = (t.cuda() for t in inputs.draw_qkv(1, 2, 1000, 128, 9800, torch.bfloat16))
+    a, b = both(gpu_lib, serial, lambda: (gpu_lib.forward_standard(q, k, v, causal=causal),))
+    assert_same(a, b)
