@@ -20,11 +20,23 @@ constexpr int kVersion = 100;  // 0.1.0
 // grid dimension of 2^32 work-items or more: that bounds B*H*ceil(N/32) below
 // 2^23, which matters only for very short sequences (N <= 2 with d = 64
 // would otherwise allow B*H up to 2^25).
+// a * b * ... < limit for positive int factors, without overflowing (each
+// partial product is checked before the next multiplication).
+template <typename... I>
+bool product_below(int64_t limit, int a, I... rest) {
+    int64_t p = a;
+    if (p >= limit) return false;
+    for (int f : {rest...}) {
+        p *= f;  // p < 2^31 and f < 2^31: no overflow
+        if (p >= limit) return false;
+    }
+    return true;
+}
+
 int check_shape(int B, int H, int N, int d, bool allow256 = false) {
     if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
     if (d != 64 && d != 128 && !(allow256 && d == 256)) return FA_ERR_HEADDIM;
-    const int64_t total = (int64_t)B * H * N * d;
-    if (total >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
+    if (!product_below((int64_t)1 << 31, B, H, N, d)) return FA_ERR_SHAPE;
     if ((int64_t)B * H * ((N + 31) / 32) >= ((int64_t)1 << 23)) return FA_ERR_SHAPE;
     return FA_OK;
 }
@@ -59,8 +71,9 @@ struct SplitPlan {
 int splitkv_shape(int B, int H, int Nq, int Nk, int d, int num_splits) {
     if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
     if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+    if (!product_below((int64_t)1 << 31, B, H, Nq, d) || !product_below((int64_t)1 << 31, B, H, Nk, d))
+        return FA_ERR_SHAPE;
     const int64_t bh = (int64_t)B * H;
-    if (bh * Nq * d >= ((int64_t)1 << 31) || bh * Nk * d >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
     // the merge and split kernels' grids: see check_shape
     if (bh * ((Nq + 31) / 32) >= ((int64_t)1 << 23)) return FA_ERR_SHAPE;
     if (num_splits < 0 || num_splits > 1024) return FA_ERR_ARG;
@@ -298,8 +311,8 @@ int fa_probe_dq_atomics(float* ws, size_t ws_bytes, int B, int H, int N, int key
     if (key_block != 128 && key_block != 256) return FA_ERR_ARG;
     if (N % key_block != 0) return FA_ERR_SHAPE;
     if (mode != 0 && mode != 1) return FA_ERR_ARG;
+    if (!product_below((int64_t)1 << 31, B, H, N, 128)) return FA_ERR_SHAPE;
     const int64_t el = (int64_t)B * H * N * 128;
-    if (el >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
     if ((int64_t)B * H * (N / key_block) * 512 >= ((int64_t)1 << 32)) return FA_ERR_SHAPE;
     if (ws_bytes < (size_t)el * sizeof(float)) return FA_ERR_WORKSPACE;
     if (((uintptr_t)ws & 255) != 0) return FA_ERR_WORKSPACE;
