@@ -476,7 +476,8 @@ struct Dkdv1Wave {
     int N, tid, lane, wave, l32, h, key0, key;
     float c;
     V8 kf[C::KS], vf[DK ? C::KS : 1];   // B operands: K (and V) rows of this lane's key
-    int ld_row[C::NLOADQ], ld_col[C::NLOADQ];
+    int ld_row[C::NLOADQ];
+    unsigned ld_cb[C::NLOADQ];          // byte offset of this thread's 16 bytes within a row
     f32x16 acc[C::DB];                  // dK^T or dV^T: head dim in registers, key = lane
 
     __device__ __forceinline__ void init(const T* Qh_, const T* Kh, const T* Vh, const T* dOh_,
@@ -509,7 +510,7 @@ struct Dkdv1Wave {
             const int byte = i * (C::NT * 16) + tid * 16;
             const int r = byte / C::ROWB, p = (byte % C::ROWB) / 16;
             ld_row[i] = r;
-            ld_col[i] = (p ^ tile_swz<D>(r)) * 8;
+            ld_cb[i] = (unsigned)(p ^ tile_swz<D>(r)) * 16u;
         }
 #pragma unroll
         for (int b = 0; b < C::DB; ++b) acc[b] = f32x16{};
@@ -519,12 +520,16 @@ struct Dkdv1Wave {
     // (the 4-byte loads fill 64 entries; rows past the block read clamped rows).
     __device__ __forceinline__ void issue(int qbase, char* sQd, char* sGd, float* sLd,
                                           float* sDd) const {
+        // 32-bit byte offsets from the head's base (a head holds < 2^31
+        // elements): no 64-bit address per load
+        const char* qb = reinterpret_cast<const char*>(Qh);
+        const char* gb = reinterpret_cast<const char*>(dOh);
 #pragma unroll
         for (int i = 0; i < C::NLOADQ; ++i) {
-            const size_t row = (size_t)min(qbase + ld_row[i], N - 1) * D;
+            const unsigned off = (unsigned)min(qbase + ld_row[i], N - 1) * (D * 2u) + ld_cb[i];
             const int o = i * (C::NT * 16) + wave * 1024;
-            __builtin_amdgcn_global_load_lds(Qh + row + ld_col[i], sQd + o, 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(dOh + row + ld_col[i], sGd + o, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(qb + off, sQd + o, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(gb + off, sGd + o, 16, 0, 0);
         }
         const int r = min(qbase + lane, N - 1);
         if (wave == 0) __builtin_amdgcn_global_load_lds(lse2h + r, sLd, 4, 0, 0);
@@ -721,7 +726,7 @@ struct DqWave {
     int N, nkt, tid, lane, wave, l32, h, q0, qrow;
     float c, lse2, del;             // del: -D of this lane's query
     V8 qf[C::KS], gf[C::KS];        // B operands: Q and dO rows of this lane's query
-    int ld_row[C::NLOAD], ld_col[C::NLOAD];
+    int ld_row[C::NLOAD];
     unsigned ld_off[C::NLOAD];      // byte offset of this thread's 16 bytes within a full tile
     int roff[C::KS];                // 16-byte row reads of K / V (key l32; +32 rows for c2 = 1)
     int toff[2][C::DB];             // transposing reads of K [half][b] (g = 0; +16 g rows)
@@ -763,8 +768,7 @@ struct DqWave {
             const int byte = i * (C::NT * 16) + tid * 16;
             const int r = byte / C::ROWB, p = (byte % C::ROWB) / 16;
             ld_row[i] = r;
-            ld_col[i] = (p ^ tile_swz<D>(r)) * 8;
-            ld_off[i] = (unsigned)(r * D + ld_col[i]) * 2u;
+            ld_off[i] = (unsigned)(r * D + (p ^ tile_swz<D>(r)) * 8) * 2u;
         }
 #pragma unroll
         for (int s = 0; s < C::KS; ++s) roff[s] = tile_off<D>(l32, 16 * s + 8 * h);
@@ -800,12 +804,16 @@ struct DqWave {
             }
             return;
         }
+        const char* kb = reinterpret_cast<const char*>(Kh);
+        const char* vb = reinterpret_cast<const char*>(Vh);
 #pragma unroll
         for (int i = 0; i < C::NLOAD; ++i) {
-            const size_t row = (size_t)min(kbase + ld_row[i], N - 1) * D;
+            // rows past N re-read row N - 1 (32-bit byte offsets, as above)
+            const unsigned off = (unsigned)min(kbase + ld_row[i], N - 1) * (D * 2u) +
+                                 (ld_off[i] - (unsigned)ld_row[i] * (D * 2u));
             const int o = i * (C::NT * 16) + wave * 1024;
-            __builtin_amdgcn_global_load_lds(Kh + row + ld_col[i], sKd + o, 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(Vh + row + ld_col[i], sVd + o, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(kb + off, sKd + o, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vb + off, sVd + o, 16, 0, 0);
         }
     }
 

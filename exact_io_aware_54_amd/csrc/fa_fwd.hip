@@ -157,13 +157,33 @@ struct FwdWave {
             }
             return;
         }
+        if constexpr (D == 128) {
+            // 64-bit addresses here: at head dim 128 the 32-bit offsets below
+            // leave the kernel 174 registers instead of 222 and it measured 5 %
+            // slower (B8 H16 N4096 causal and B2 H32 N8192); at 64 and 256 they
+            // are 5 % and 1 % faster
 #pragma unroll
-        for (int i = 0; i < C::NLOAD; ++i) {
-            const size_t row = (size_t)min(kbase + ld_row[i], N - 1) * D;
-            char* kdst = sKd + i * (C::NT * 16) + wave * 1024;
-            char* vdst = sVd + i * (C::NT * 16) + wave * 1024;  // this wave's 1 KiB of load i
-            __builtin_amdgcn_global_load_lds(Kh + row + ld_col[i], kdst, 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(Vh + row + ld_col[i], vdst, 16, 0, 0);
+            for (int i = 0; i < C::NLOAD; ++i) {
+                const size_t row = (size_t)min(kbase + ld_row[i], N - 1) * D;
+                char* kdst = sKd + i * (C::NT * 16) + wave * 1024;
+                char* vdst = sVd + i * (C::NT * 16) + wave * 1024;  // this wave's 1 KiB of load i
+                __builtin_amdgcn_global_load_lds(Kh + row + ld_col[i], kdst, 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(Vh + row + ld_col[i], vdst, 16, 0, 0);
+            }
+        } else {
+            const char* kb = reinterpret_cast<const char*>(Kh);
+            const char* vb = reinterpret_cast<const char*>(Vh);
+#pragma unroll
+            for (int i = 0; i < C::NLOAD; ++i) {
+                // 32-bit byte offsets from the head's base (a head holds < 2^31
+                // elements)
+                const unsigned off = (unsigned)min(kbase + ld_row[i], N - 1) * (D * 2u) +
+                                     (ld_off[i] - (unsigned)ld_row[i] * (D * 2u));
+                char* kdst = sKd + i * (C::NT * 16) + wave * 1024;
+                char* vdst = sVd + i * (C::NT * 16) + wave * 1024;
+                __builtin_amdgcn_global_load_lds(kb + off, kdst, 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(vb + off, vdst, 16, 0, 0);
+            }
         }
     }
 
