@@ -297,6 +297,9 @@ def run_suite(path, torch, fa, inputs):
         ("bwd bf16 B1 H32 N8192 d256 (non-causal)", "bwd", torch.bfloat16, 1, 32, 8192, 256,
          False, "causal_8k"),
         ("fwd fp8 B2 H32 N8192 d128", "fp8", None, 2, 32, 8192, 128, False, "fp8_8k"),
+        ("fwd fp8 causal B2 H32 N8192 d128", "fp8", None, 2, 32, 8192, 128, True, "fp8_8k"),
+        # the fp8 backward widens the codes and runs the 16-bit passes: bf16 peak
+        ("bwd fp8 B2 H32 N8192 d128", "fp8bwd", None, 2, 32, 8192, 128, False, "fp8_8k"),
         ("fwd f32 B1 H2 N128 d64", "fwd", torch.float32, 1, 2, 128, 64, False, "tiny_f32"),
     ]
     out = open(path, "w")
@@ -311,6 +314,19 @@ def run_suite(path, torch, fa, inputs):
             lse = torch.empty((B, H, N), device="cuda", dtype=torch.float32)
             fn = lambda: fa.fa_fwd_fp8(q8, k8, v8, sc[0], sc[1], sc[2], o, lse, scale, causal)  # noqa
             flops, peak = counted_flops(B, H, N, d, causal), PEAK_FP8_TFLOPS
+        elif kind == "fp8bwd":
+            (q8, k8, v8), sc = inputs.draw_fp8(B, H, N, d, seed)
+            q8, k8, v8 = q8.cuda(), k8.cuda(), v8.cuda()
+            o, lse = fa.forward_fp8(q8, k8, v8, sc, scale=scale, causal=causal)
+            g = torch.Generator().manual_seed(seed + 1)
+            do = torch.randn((B, H, N, d), generator=g).to(torch.bfloat16).cuda()
+            dq, dk, dv = (torch.empty((B, H, N, d), device="cuda", dtype=torch.bfloat16)
+                          for _ in range(3))
+            ws = torch.empty(fa.fa_bwd_fp8_workspace_bytes(B, H, N, d), device="cuda",
+                             dtype=torch.uint8)
+            fn = lambda: fa.fa_bwd_fp8(q8, k8, v8, sc[0], sc[1], sc[2], o, lse, do, dq, dk, dv,  # noqa
+                                       ws, scale, causal)
+            flops, peak = counted_flops(B, H, N, d, causal, backward=True), PEAK_BF16_TFLOPS
         else:
             q, k, v, do = (t.cuda() for t in inputs.draw_qkv(B, H, N, d, seed, dt, with_do=True))
             o = torch.empty_like(q)
