@@ -210,6 +210,19 @@ def test_bwd_d256_small(gpu_lib, dtype, causal, N):
         assert rel_frob(got, exp) <= 1e-2
 
 
+def test_bwd_d256_noncausal_ragged(gpu_lib):
+    """Head dim 256 without the mask over many tiles with a ragged end (N = 1000:
+    15 full 64-row tiles and one of 40): the dQ pass takes the two 32-key halves
+    one after the other there, and every Q / dO load of the split dK / dV
+    launches and the ragged K / V loads use 32-bit offsets from the head base."""
+    B, H, N, d = 1, 4, 1000, 256
+    note(f"bwd bf16 non-causal B{B} H{H} N{N} d{d}")
+    (dq, dk, dv), ref = check_bwd_full(gpu_lib, "bf16", B, H, N, d, False, 8700)
+    for got, exp in zip((dq, dk, dv), ref):
+        assert max_abs(got, exp) <= 5e-2
+        assert rel_frob(got, exp) <= 1e-2
+
+
 def test_bwd_d256_workload(gpu_lib):
     """Head dim 256 backward at a training-like shape, every element of two heads."""
     B, H, N, d = 2, 8, 2048, 256
