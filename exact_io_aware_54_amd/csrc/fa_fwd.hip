@@ -222,10 +222,13 @@ struct FwdWave {
                 __builtin_amdgcn_sched_barrier(0);
             }
         } else {
+            // one subtile's k-steps after the other (same accumulation order
+            // as k-steps outside, bit-identical): 1-1.5 % faster at d = 64 and
+            // 128 than alternating the two subtiles
 #pragma unroll
-            for (int ks = 0; ks < C::KS; ++ks)
+            for (int c2 = 0; c2 < C::NSUB; ++c2)
 #pragma unroll
-                for (int c2 = 0; c2 < C::NSUB; ++c2) {
+                for (int ks = 0; ks < C::KS; ++ks) {
                     const V8 a = *reinterpret_cast<const V8*>(kb + koff[ks] + c2 * 32 * C::ROWB);
                     s[c2] = mfma32(a, qf[ks], s[c2]);
                 }
