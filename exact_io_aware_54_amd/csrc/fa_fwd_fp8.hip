@@ -148,10 +148,12 @@ struct Fp8Wave {
         f32x16 s[F8_NSUB];
 #pragma unroll
         for (int c2 = 0; c2 < F8_NSUB; ++c2) s[c2] = f32x16{};
+        // one subtile's two k-steps after the other (bit-identical; ~0.8 %
+        // faster on C5 than alternating the subtiles per k-step)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+        for (int c2 = 0; c2 < F8_NSUB; ++c2)
 #pragma unroll
-            for (int c2 = 0; c2 < F8_NSUB; ++c2) {
+            for (int ks = 0; ks < 2; ++ks) {
                 const i32x4 lo = *reinterpret_cast<const i32x4*>(kb + koff[ks][0] + c2 * 32 * F8_D);
                 const i32x4 hi = *reinterpret_cast<const i32x4*>(kb + koff[ks][1] + c2 * 32 * F8_D);
                 const i32x8 a{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
