@@ -7,6 +7,9 @@
 (2) Peaked rows: scale = 1 instead of 1/sqrt(d), scores of standard
     deviation ~sqrt(d), so most rows are close to one-hot and exponents span
     hundreds of units.
+(3) Flat rise: the keys after the first tile score uniformly higher, so a
+    tile's sum of probabilities can pass the refresh threshold without any
+    single probability passing it.
 Tolerances are the 16-bit ones: O max-abs <= 2e-2 and relative Frobenius <=
 1e-2, LSE max-abs <= 1e-3 (|LSE| reaches ~40 here and the scores are exact
 products of the rounded inputs accumulated in fp32), dQ/dK/dV relative
@@ -33,15 +36,18 @@ def note(msg):
     print(f"\n[case] {msg}", flush=True)
 
 
-def check(fa, q, k, v, do, scale, causal):
+def check(fa, q, k, v, do, scale, causal, grads=True):
     qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
     o, lse = fa.forward(qd, kd, vd, scale=scale, causal=causal)
-    grads = fa.backward(qd, kd, vd, o, lse, dod, scale=scale, causal=causal)
     torch.cuda.synchronize()
     o_ref, l_ref = oracle.attention_forward(to64(q), to64(k), to64(v), scale, causal)
     assert np.all(np.isfinite(to64(o))) and np.all(np.isfinite(to64(lse)))
     assert max_abs(to64(o), o_ref) <= 2e-2 and rel_frob(to64(o), o_ref) <= 1e-2
     assert max_abs(to64(lse), l_ref) <= 1e-3
+    if not grads:
+        return
+    grads = fa.backward(qd, kd, vd, o, lse, dod, scale=scale, causal=causal)
+    torch.cuda.synchronize()
     refs = oracle.attention_backward(to64(q), to64(k), to64(v), to64(do), scale, causal)
     for name, g, r in zip("QKV", grads, refs):
         g = to64(g)
@@ -68,3 +74,29 @@ def test_peaked_rows(gpu_lib, d, causal):
     note(f"peaked rows (scale 1) bf16 B{B} H{H} N{N} d{d} causal={causal}")
     q, k, v, do = inputs.draw_qkv(B, H, N, d, 9500 + d, torch.bfloat16, with_do=True)
     check(gpu_lib, q, k, v, do, 1.0, causal)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("rise", [3.5, 9.0])
+def test_flat_rise(gpu_lib, d, causal, rise):
+    """(3) Every key after the first 64 scores `rise` log2 units above the
+    first 64 (which score 0), plus small noise: at rise 3.5 a lane's sum of
+    probabilities over a tile passes 2^8 while no single one does (the
+    head-dim-64 forward then re-forms the tile's scores but must not move its
+    reference); at rise 9 each later probability passes 2^8 and the reference
+    must move. Forward only: dQ's first component here is the one large key
+    component times a sum of dS over the later keys that cancels to a small
+    fraction of its terms, so the 2^-9 rounding of each 16-bit dS dominates
+    it (5e-2 relative measured), whatever the kernel."""
+    B, H, N = 1, 2, 300
+    note(f"flat rise {rise} bf16 B{B} H{H} N{N} d{d} causal={causal}")
+    q, k, v, do = inputs.draw_qkv(B, H, N, d, 9600 + d, torch.float32, with_do=True)
+    scale = d ** -0.5
+    q = 0.05 * q
+    q[..., 0] = 1.0
+    k = 0.05 * k
+    k[..., 0] = 0.0
+    k[:, :, 64:, 0] = rise / (scale * np.log2(np.e))
+    q, k, v, do = (t.to(torch.bfloat16) for t in (q, k, v, do))
+    check(gpu_lib, q, k, v, do, scale, causal, grads=False)
