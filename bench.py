@@ -185,6 +185,18 @@ def time_launches(fns, steps, warmup, torch):
     return wall, per
 
 
+def calibration_copy(torch):
+    """A plain device copy of known size (reads and writes exactly 1 GiB,
+    three times): the HBM counters of a profiled run are scaled by what they
+    read for it."""
+    src = torch.ones(1 << 28, device="cuda", dtype=torch.float32)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def run_main(args):
     import torch
     import exact_io_aware_54_amd as fa
@@ -192,13 +204,7 @@ def run_main(args):
 
     fa.load_library()
     if args.calibrate_copy:
-        # a plain copy of known size: reads and writes exactly 1 GiB each
-        src = torch.ones(1 << 28, device="cuda", dtype=torch.float32)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calibration_copy(torch)
     B, H, N, d, causal = 8, 16, 4096, 128, True
     scale = 1.0 / math.sqrt(d)
     print(f"[bench] drawing inputs B{B} H{H} N{N} d{d}", file=sys.stderr, flush=True)
@@ -503,9 +509,11 @@ def run_loop_order(path, torch, fa, inputs):
     out.close()
 
 
-def run_tile_sweep(path, torch, fa, inputs):
+def run_tile_sweep(path, torch, fa, inputs, calibrate=False):
     """The forward's two workgroup shapes (four and eight waves) on each bf16
     forward workload, medians of 20 event-timed launches after the warm-up."""
+    if calibrate:
+        calibration_copy(torch)
     cases = [("C2", 4, 16, 2048, 64, False, 1002), ("C3a", 1, 32, 8192, 128, True, 1003),
              ("C3b", 1, 32, 16384, 128, True, 1013), ("C4", 8, 16, 4096, 128, True, 1004),
              ("non-causal", 2, 32, 8192, 128, False, 1005)]
@@ -607,12 +615,7 @@ def run_fp8(path, torch, fa, inputs, calibrate=False):
     x20 outliers), non-causal (the graded case) and causal: medians of 20
     event-timed launches after at least 60 ms of warm-up, one JSON line each."""
     if calibrate:
-        src = torch.ones(1 << 28, device="cuda", dtype=torch.float32)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calibration_copy(torch)
     B, H, N, d = 2, 32, 8192, 128
     seed = inputs.SEEDS["fp8_8k"]
     (q8, k8, v8), sc = inputs.draw_fp8(B, H, N, d, seed)
@@ -690,7 +693,7 @@ def main():
         if args.loop_order:
             run_loop_order(args.loop_order, torch, fa, inputs)
         if args.tile_sweep:
-            run_tile_sweep(args.tile_sweep, torch, fa, inputs)
+            run_tile_sweep(args.tile_sweep, torch, fa, inputs, args.calibrate_copy)
         if args.compare_standard:
             run_compare(args.compare_standard, torch, fa, inputs, args.compare_n)
         if args.fp8:
