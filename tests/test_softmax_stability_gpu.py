@@ -76,10 +76,11 @@ def test_peaked_rows(gpu_lib, d, causal):
     check(gpu_lib, q, k, v, do, 1.0, causal)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("rise", [3.5, 9.0])
-def test_flat_rise(gpu_lib, d, causal, rise):
+def test_flat_rise(gpu_lib, d, causal, rise, dtype):
     """(3) Every key after the first 64 scores `rise` log2 units above the
     first 64 (which score 0), plus small noise: at rise 3.5 a lane's sum of
     probabilities over a tile passes 2^8 while no single one does (the
@@ -90,7 +91,7 @@ def test_flat_rise(gpu_lib, d, causal, rise):
     fraction of its terms, so the 2^-9 rounding of each 16-bit dS dominates
     it (5e-2 relative measured), whatever the kernel."""
     B, H, N = 1, 2, 300
-    note(f"flat rise {rise} bf16 B{B} H{H} N{N} d{d} causal={causal}")
+    note(f"flat rise {rise} {str(dtype)[6:]} B{B} H{H} N{N} d{d} causal={causal}")
     q, k, v, do = inputs.draw_qkv(B, H, N, d, 9600 + d, torch.float32, with_do=True)
     scale = d ** -0.5
     q = 0.05 * q
@@ -98,5 +99,5 @@ def test_flat_rise(gpu_lib, d, causal, rise):
     k = 0.05 * k
     k[..., 0] = 0.0
     k[:, :, 64:, 0] = rise / (scale * np.log2(np.e))
-    q, k, v, do = (t.to(torch.bfloat16) for t in (q, k, v, do))
+    q, k, v, do = (t.to(dtype) for t in (q, k, v, do))
     check(gpu_lib, q, k, v, do, scale, causal, grads=False)
