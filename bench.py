@@ -58,6 +58,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16/fp16 MFMA
 PEAK_FP8_TFLOPS = 5033.2    # MI355X dense fp8 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X dense fp32 MFMA
 KERNEL_SOURCES = {
     "fwd_mfma_kernel": "exact_io_aware_54_amd/csrc/fa_fwd.hip",
     "bwd_dkdv_kernel": "exact_io_aware_54_amd/csrc/fa_bwd.hip",
@@ -307,6 +308,9 @@ def run_suite(path, torch, fa, inputs):
         # the fp8 backward widens the codes and runs the 16-bit passes: bf16 peak
         ("bwd fp8 B2 H32 N8192 d128", "fp8bwd", None, 2, 32, 8192, 128, False, "fp8_8k"),
         ("fwd f32 B1 H2 N128 d64", "fwd", torch.float32, 1, 2, 128, 64, False, "tiny_f32"),
+        ("fwd f32 B4 H16 N2048 d64", "fwd", torch.float32, 4, 16, 2048, 64, False, "fwd_bf16"),
+        ("fwd f32 causal B1 H32 N4096 d128", "fwd", torch.float32, 1, 32, 4096, 128, True,
+         "causal_8k"),
     ]
     out = open(path, "w")
     for name, kind, dt, B, H, N, d, causal, seedkey in cases:
@@ -346,7 +350,7 @@ def run_suite(path, torch, fa, inputs):
                 ws = fa.workspace_for(q)
                 fn = lambda: fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, scale, causal)  # noqa
                 flops = counted_flops(B, H, N, d, causal, backward=True)
-            peak = PEAK_BF16_TFLOPS
+            peak = PEAK_FP32_TFLOPS if dt == torch.float32 else PEAK_BF16_TFLOPS
         warm_up(fn, torch)
         times = []
         for _ in range(20):
@@ -644,6 +648,49 @@ def run_fp8(path, torch, fa, inputs, calibrate=False):
     out.close()
 
 
+F32_CASES = [
+    # (name, B, H, N, d, causal, seed key)
+    ("fwd f32 B1 H2 N128 d64", 1, 2, 128, 64, False, "tiny_f32"),
+    ("fwd f32 B4 H16 N2048 d64", 4, 16, 2048, 64, False, "fwd_bf16"),
+    ("fwd f32 causal B1 H32 N4096 d128", 1, 32, 4096, 128, True, "causal_8k"),
+    ("fwd f32 B1 H32 N4096 d128", 1, 32, 4096, 128, False, "causal_8k"),
+]
+
+
+def run_f32(path, torch, fa, inputs, calibrate=False):
+    """The fp32 forward alone: the tiny parity workload and longer shapes,
+    medians of 20 event-timed launches after at least 60 ms of warm-up, one
+    JSON line each, against the fp32 MFMA peak."""
+    if calibrate:
+        calibration_copy(torch)
+    out = open(path, "w")
+    for name, B, H, N, d, causal, seedkey in F32_CASES:
+        seed = inputs.SEEDS[seedkey]
+        q, k, v = (t.cuda() for t in inputs.draw_qkv(B, H, N, d, seed, torch.float32))
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), device="cuda", dtype=torch.float32)
+        fn = lambda: fa.fa_fwd(q, k, v, o, lse, d ** -0.5, causal)  # noqa: E731
+        warm_up(fn, torch)
+        times = []
+        for _ in range(20):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        med = sorted(times)[len(times) // 2]
+        flops = counted_flops(B, H, N, d, causal)
+        rec = {"workload": name, "seed": seed, "median_ms": round(med, 4),
+               "tflops": round(flops / (med * 1e-3) / 1e12, 2),
+               "frac_fp32_peak": round(flops / (med * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4)}
+        print(json.dumps(rec), file=out, flush=True)
+        print(f"[f32] {json.dumps(rec)}", file=sys.stderr, flush=True)
+        del q, k, v, o, lse, fn
+        torch.cuda.empty_cache()
+    out.close()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -664,6 +711,8 @@ def main():
     ap.add_argument("--tile-sweep", metavar="PATH",
                     help="only time the forward's four- and eight-wave workgroup shapes on each "
                          "bf16 forward workload, JSON lines to PATH")
+    ap.add_argument("--f32", metavar="PATH",
+                    help="only time the fp32 forward (tiny and longer shapes), JSON lines to PATH")
     ap.add_argument("--fp8", metavar="PATH",
                     help="only time the fp8 forward on its workload (causal and not), JSON lines "
                          "to PATH")
@@ -681,7 +730,7 @@ def main():
               "the per-GPU head count; run with --gpus 1.", file=sys.stderr, flush=True)
         sys.exit(2)
     if (args.decode or args.compare_standard or args.loop_order or args.tile_sweep or args.fp8
-            or args.bwd_design):
+            or args.bwd_design or args.f32):
         import torch
         import exact_io_aware_54_amd as fa
         from exact_io_aware_54_amd import inputs
@@ -698,6 +747,8 @@ def main():
             run_compare(args.compare_standard, torch, fa, inputs, args.compare_n)
         if args.fp8:
             run_fp8(args.fp8, torch, fa, inputs, args.calibrate_copy)
+        if args.f32:
+            run_f32(args.f32, torch, fa, inputs, args.calibrate_copy)
         if args.bwd_design:
             run_bwd_design(args.bwd_design, torch, fa, inputs)
         return

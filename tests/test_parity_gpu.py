@@ -60,12 +60,32 @@ def check_fwd_full(fa, dtype, B, H, N, d, causal, seed, scale=None):
 # ------------------------------------------------------------------ fp32 path
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("d,N", [(64, 128), (128, 77), (64, 1), (128, 200)])
+@pytest.mark.parametrize("d,N", [(64, 128), (128, 77), (64, 1), (128, 200), (64, 300), (128, 513)])
 def test_fwd_f32(gpu_lib, d, N, causal):
     seed = inputs.SEEDS["tiny_f32"] if (d, N) == (64, 128) else 2000 + N
     o, lse, o_ref, l_ref = check_fwd_full(gpu_lib, "f32", 1, 2, N, d, causal, seed)
     assert max_abs(o, o_ref) <= 1e-5
     assert max_abs(lse, l_ref) <= 1e-5
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_f32_long(gpu_lib, causal):
+    """fp32 over 128 key tiles and 32 query blocks per head: sampled rows of
+    every head against the float64 oracle at the fp32 bound."""
+    B, H, N, d = 1, 4, 4096, 128
+    seed = 2100 + int(causal)
+    note(f"fwd f32 B{B} H{H} N{N} d{d} causal={causal} seed={seed}")
+    q, k, v = inputs.draw_qkv(B, H, N, d, seed, torch.float32)
+    o, lse = gpu_lib.forward(*dev(q, k, v), scale=d ** -0.5, causal=causal)
+    torch.cuda.synchronize()
+    o64, l64 = to64(o), to64(lse)
+    rng = np.random.default_rng(seed)
+    for h in range(H):
+        rows = _sample_rows(N, rng)
+        o_ref, l_ref = oracle.attention_forward_rows(to64(q[0, h]), to64(k[0, h]), to64(v[0, h]),
+                                                     rows, d ** -0.5, causal)
+        assert max_abs(o64[0, h, rows], o_ref) <= 1e-5, h
+        assert max_abs(l64[0, h, rows], l_ref) <= 1e-5, h
 
 
 # ------------------------------------------------- 16-bit forward, small shapes

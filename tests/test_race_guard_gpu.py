@@ -1,8 +1,9 @@
 """Race guard: the product library against its serial-staging build, bit for bit.
 
-Every kernel that streams tiles through LDS (K/V in the forward passes, the
-split-KV forward, the standard baseline's P V pass and the dQ pass; Q/dO with
-their LSE and D rows in the dK/dV passes) double-buffers them: the loads of
+Every kernel that streams tiles through LDS (K/V in the forward passes,
+the fp32 one included, the split-KV forward, the standard baseline's P V
+pass and the dQ pass; Q/dO with their LSE and D rows in the dK/dV passes)
+double-buffers them: the loads of
 tile i+1 land in the second buffer set while tile i is computed on, and only
 a wait for the wave's own loads plus a workgroup barrier separate a tile's
 arrival from its first read and its last read from its next overwrite. The
@@ -71,6 +72,15 @@ def test_forward(gpu_lib, serial, d, waves, causal, N):
     note(f"race guard fwd bf16 B1 H3 N{N} d{d} waves={waves} causal={causal}")
     q, k, v = (t.cuda() for t in inputs.draw_qkv(1, 3, N, d, 9100 + N + d, torch.bfloat16))
     a, b = both(gpu_lib, serial, lambda: fwd_waves(gpu_lib, q, k, v, causal, waves))
+    assert_same(a, b)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_f32(gpu_lib, serial, d, causal):
+    note(f"race guard fwd f32 B1 H3 N1000 d{d} causal={causal}")
+    q, k, v = (t.cuda() for t in inputs.draw_qkv(1, 3, 1000, d, 9150 + d, torch.float32))
+    a, b = both(gpu_lib, serial, lambda: gpu_lib.forward(q, k, v, causal=causal))
     assert_same(a, b)
 
 
