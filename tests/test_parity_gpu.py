@@ -70,9 +70,10 @@ def test_fwd_f32(gpu_lib, d, N, causal):
 
 @pytest.mark.parametrize("causal", [False, True])
 def test_fwd_f32_long(gpu_lib, causal):
-    """fp32 over 128 key tiles and 32 query blocks per head: sampled rows of
-    every head against the float64 oracle at the fp32 bound."""
-    B, H, N, d = 1, 4, 4096, 128
+    """fp32 over 128 key tiles per head in the eight-wave shape (B*H*N/256 =
+    256 workgroups): sampled rows of four heads against the float64 oracle
+    at the fp32 bound."""
+    B, H, N, d = 1, 16, 4096, 128
     seed = 2100 + int(causal)
     note(f"fwd f32 B{B} H{H} N{N} d{d} causal={causal} seed={seed}")
     q, k, v = inputs.draw_qkv(B, H, N, d, seed, torch.float32)
@@ -80,7 +81,7 @@ def test_fwd_f32_long(gpu_lib, causal):
     torch.cuda.synchronize()
     o64, l64 = to64(o), to64(lse)
     rng = np.random.default_rng(seed)
-    for h in range(H):
+    for h in (0, 5, 10, 15):
         rows = _sample_rows(N, rng)
         o_ref, l_ref = oracle.attention_forward_rows(to64(q[0, h]), to64(k[0, h]), to64(v[0, h]),
                                                      rows, d ** -0.5, causal)

@@ -75,11 +75,12 @@ def test_forward(gpu_lib, serial, d, waves, causal, N):
     assert_same(a, b)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d,H,N", [(64, 3, 1000), (128, 3, 1000), (128, 64, 1056)])
 @pytest.mark.parametrize("causal", [False, True])
-def test_forward_f32(gpu_lib, serial, d, causal):
-    note(f"race guard fwd f32 B1 H3 N1000 d{d} causal={causal}")
-    q, k, v = (t.cuda() for t in inputs.draw_qkv(1, 3, 1000, d, 9150 + d, torch.float32))
+def test_forward_f32(gpu_lib, serial, d, H, N, causal):
+    # H3 N1000: four-wave workgroups; H64 N1056 (320 workgroups): eight-wave
+    note(f"race guard fwd f32 B1 H{H} N{N} d{d} causal={causal}")
+    q, k, v = (t.cuda() for t in inputs.draw_qkv(1, H, N, d, 9150 + d, torch.float32))
     a, b = both(gpu_lib, serial, lambda: gpu_lib.forward(q, k, v, causal=causal))
     assert_same(a, b)
 
