@@ -55,14 +55,29 @@ mfma_probe_kernel(unsigned long long* __restrict__ sink, int iters) {
 // workgroup of eight waves per (head, block of KB keys), stepping over the
 // 64-query blocks (causal: from the block holding the first key on); wave w
 // adds the 32 x 32 block (query half w / 4, head-dim block w % 4) in the MFMA
-// accumulator layout (16 floats per lane, lanes along the head dim). MODE 0
-// uses float atomic adds (device scope), MODE 1 plain stores of the same
-// addresses (the write bandwidth of the pattern). Its time is a lower bound on
-// what the atomics add to a one-pass dK/dV pass.
+// accumulator layout (16 floats per lane, lanes along the head dim). Block
+// ids map to (head, key block) as in the dK/dV pass (causal: groups of at most
+// two heads per XCD, longest blocks first; otherwise whole heads per XCD), so
+// every partial of a head comes from one XCD. MODE 0 uses float atomic adds,
+// MODE 1 plain stores of the same addresses (the write bandwidth of the
+// pattern). Its time is a lower bound on what the atomics add to a one-pass
+// dK/dV pass. (On gfx950 the relaxed float add compiles to the same
+// instruction at workgroup and at agent scope, and it is performed past the
+// XCD's L2 either way: the sums come out exact even when a head's blocks are
+// spread over XCDs, at the same ~1.3 TB/s of payload.)
 template <int MODE>
 __device__ __forceinline__ void dq_probe_body(float* __restrict__ ws, int N, int nkb, int kb_rows,
                                               int causal) {
-    const int bh = blockIdx.x / nkb, kb = blockIdx.x % nkb;
+    const int BH = gridDim.x / nkb;
+    int bh, kb;
+    if (causal) {
+        causal_block(blockIdx.x, nkb, BH, bh, kb, 2);
+        kb = nkb - 1 - kb;
+    } else {
+        const int L = xcd_remap(blockIdx.x, BH * nkb);
+        bh = L / nkb;
+        kb = L % nkb;
+    }
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int l32 = lane & 31, h = lane >> 5;
     const int qsub = wave >> 2, db = wave & 3;

@@ -359,9 +359,10 @@ int fa_probe_mfma(unsigned long long* sink, int blocks, int iters, hipStream_t s
  * ("11.11 Flash Attention", section "The Recomputation Trade-off": every
  * (key block, query block) pair contributes to dQ of that query block). For
  * head dim 128 it issues exactly that stream of additions and nothing else:
- * one workgroup per (batch*head, block of key_block keys), one 64 x 128 float
- * partial per 64-query step (causal != 0: steps from the key block's first
- * query block on), added with device-scope float atomics (mode 0) or written
+ * one workgroup per (batch*head, block of key_block keys), placed on the XCDs
+ * as the dK/dV pass places its blocks, one 64 x 128 float partial per
+ * 64-query step (causal != 0: steps from the key block's first query block
+ * on), added with device-scope float atomics (mode 0) or written
  * with plain stores to the same addresses (mode 1). Its duration is a lower
  * bound on what the atomics would add to such a pass.
  *   ws         [B*H*N*128] float32 device buffer, 256-byte aligned; its
