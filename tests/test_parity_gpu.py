@@ -173,12 +173,13 @@ def _sample_rows(n, rng, extra=24):
     return np.unique(np.clip(np.concatenate([fixed, rnd]), 0, n - 1))
 
 
-@pytest.mark.parametrize("N,seed", [(8192, inputs.SEEDS["causal_8k"]),
-                                    (16384, inputs.SEEDS["causal_16k"])])
-def test_fwd_bf16_causal_long(gpu_lib, N, seed):
+@pytest.mark.parametrize("N,seed,dtype", [(8192, inputs.SEEDS["causal_8k"], "bf16"),
+                                          (16384, inputs.SEEDS["causal_16k"], "bf16"),
+                                          (8192, inputs.SEEDS["causal_8k"], "f16")])
+def test_fwd_bf16_causal_long(gpu_lib, N, seed, dtype):
     B, H, d = 1, 32, 128
-    note(f"fwd bf16 causal B{B} H{H} N{N} d{d} seed={seed}")
-    q, k, v = inputs.draw_qkv(B, H, N, d, seed, torch.bfloat16)
+    note(f"fwd {dtype} causal B{B} H{H} N{N} d{d} seed={seed}")
+    q, k, v = inputs.draw_qkv(B, H, N, d, seed, DT[dtype])
     o, lse = gpu_lib.forward(*dev(q, k, v), scale=d ** -0.5, causal=True)
     torch.cuda.synchronize()
     o64, l64 = to64(o), to64(lse)
@@ -287,13 +288,15 @@ def test_bwd_noncausal_wide_launch(gpu_lib, d):
             assert rel_frob(to64(got[b, h]), exp) <= 1e-2, (name, b, h)
 
 
-def test_fwd_bwd_training_workload(gpu_lib):
-    """B8 H16 N4096 d128 causal bf16: the shape the benchmark times."""
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_fwd_bwd_training_workload(gpu_lib, dtype):
+    """B8 H16 N4096 d128 causal: the shape the benchmark times (bf16), and the
+    same launch configuration with fp16 inputs."""
     B, H, N, d = 8, 16, 4096, 128
     seed = inputs.SEEDS["train_4k"]
     scale = d ** -0.5
-    note(f"fwd+bwd bf16 causal B{B} H{H} N{N} d{d} seed={seed}")
-    q, k, v, do = inputs.draw_qkv(B, H, N, d, seed, torch.bfloat16, with_do=True)
+    note(f"fwd+bwd {dtype} causal B{B} H{H} N{N} d{d} seed={seed}")
+    q, k, v, do = inputs.draw_qkv(B, H, N, d, seed, DT[dtype], with_do=True)
     qd, kd, vd, dod = dev(q, k, v, do)
     o, lse = gpu_lib.forward(qd, kd, vd, scale=scale, causal=True)
     dq, dk, dv = gpu_lib.backward(qd, kd, vd, o, lse, dod, scale=scale, causal=True)
