@@ -38,6 +38,9 @@ causal and not), one JSON line per case.
 `--bwd-design PATH` times the two-pass backward's launches on the training
 workload against the dQ float atomics a one-pass backward would add
 (fa_probe_dq_atomics), one JSON line per measurement.
+`--sweep PATH` times the forward and the whole backward over sequence lengths
+1K to 32K at the training workload's token count (bf16, d=128, H=16,
+B = 32768 / N), causal and not, one JSON line per (N, causal, pass).
 `--compare-standard PATH` runs only the comparison of the IO-aware forward with
 the standard (materialising) forward that the pages' exercise describes
 (B=1, H=32, d=128, fp16 random normals, N = 2048, 8192, 32768; at least 60 ms
@@ -367,6 +370,52 @@ def run_suite(path, torch, fa, inputs):
         print(json.dumps(rec), file=out, flush=True)
         print(f"[suite] {json.dumps(rec)}", file=sys.stderr, flush=True)
         del fn
+        torch.cuda.empty_cache()
+    out.close()
+
+
+def run_sweep(path, torch, fa, inputs, lengths=(1024, 2048, 4096, 8192, 16384, 32768)):
+    """Sequence-length sweep at a fixed token count: bf16, d = 128, H = 16, B = 32768 / N
+    (the training workload's B*N), causal and not. The forward and the whole backward
+    (fa_bwd: row terms, dK/dV pass, dQ pass), medians of 20 HIP-event-timed calls after
+    at least 60 ms of warm-up each, one JSON line per (N, causal, pass)."""
+    import statistics
+    H, d = 16, 128
+    scale = d ** -0.5
+    out = open(path, "w")
+    for N in lengths:
+        B = max(1, 32768 // N)
+        q, k, v, do = (t.cuda() for t in inputs.draw_qkv(B, H, N, d, inputs.SEEDS["train_4k"],
+                                                          torch.bfloat16, with_do=True))
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), device="cuda", dtype=torch.float32)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = fa.workspace_for(q)
+        for causal in (True, False):
+            fa.fa_fwd(q, k, v, o, lse, scale, causal)
+            passes = (("fwd", lambda: fa.fa_fwd(q, k, v, o, lse, scale, causal)),  # noqa
+                      ("bwd", lambda: fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, scale,  # noqa
+                                                causal)))
+            for pname, fn in passes:
+                print(f"[sweep] N{N} B{B} causal={causal} {pname}", file=sys.stderr, flush=True)
+                warm_up(fn, torch)
+                times = []
+                for _ in range(20):
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    fn()
+                    e1.record()
+                    torch.cuda.synchronize()
+                    times.append(e0.elapsed_time(e1))
+                med = statistics.median(times)
+                flops = counted_flops(B, H, N, d, causal, backward=(pname == "bwd"))
+                tf = flops / (med * 1e-3) / 1e12
+                rec = {"pass": pname, "B": B, "H": H, "N": N, "d": d, "causal": causal,
+                       "median_ms": round(med, 4), "tflops": round(tf, 1),
+                       "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+                print(json.dumps(rec), file=out, flush=True)
+        del q, k, v, do, o, lse, dq, dk, dv, ws
         torch.cuda.empty_cache()
     out.close()
 
@@ -719,6 +768,9 @@ def main():
     ap.add_argument("--bwd-design", metavar="PATH",
                     help="only time the two-pass backward's launches against the dQ float "
                          "atomics a one-pass backward would add, JSON lines to PATH")
+    ap.add_argument("--sweep", metavar="PATH",
+                    help="only run the sequence-length sweep (bf16 d128, B*N = 32768, forward "
+                         "and backward, causal and not), JSON lines to PATH")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device copy, the reference kernel for scaling "
                          "PMC byte counters")
@@ -730,7 +782,7 @@ def main():
               "the per-GPU head count; run with --gpus 1.", file=sys.stderr, flush=True)
         sys.exit(2)
     if (args.decode or args.compare_standard or args.loop_order or args.tile_sweep or args.fp8
-            or args.bwd_design or args.f32):
+            or args.bwd_design or args.f32 or args.sweep):
         import torch
         import exact_io_aware_54_amd as fa
         from exact_io_aware_54_amd import inputs
@@ -751,6 +803,8 @@ def main():
             run_f32(args.f32, torch, fa, inputs, args.calibrate_copy)
         if args.bwd_design:
             run_bwd_design(args.bwd_design, torch, fa, inputs)
+        if args.sweep:
+            run_sweep(args.sweep, torch, fa, inputs)
         return
     run_main(args)
 

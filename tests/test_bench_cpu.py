@@ -41,5 +41,5 @@ def test_help_lists_modes():
                        timeout=120)
     assert r.returncode == 0
     for flag in ("--steps", "--warmup", "--suite", "--fp8", "--tile-sweep", "--decode",
-                 "--loop-order", "--compare-standard", "--calibrate-copy"):
+                 "--loop-order", "--compare-standard", "--calibrate-copy", "--sweep"):
         assert flag in r.stdout
