@@ -20,15 +20,20 @@
 //     then dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read straight
 //     out of the row-major Q / dO tiles by transposing LDS reads. The two
 //     waves sharing a key group sum their partials through LDS at the end.
-//  3. bwd_dq: one workgroup per (batch*head, block of 128 queries), shaped
-//     like the forward: Q and dO rows of the wave's 32 queries stay in
+//  3. bwd_dq: one workgroup per (batch*head, block of 256 queries, eight
+//     wavefronts; 128 queries and four wavefronts when a launch would have
+//     fewer than 256 such workgroups, and at head dim 256), shaped like the
+//     forward: Q and dO rows of the wave's 32 queries stay in
 //     registers, K/V tiles stream through LDS; per tile S^T = K Q^T,
 //     dP^T = V dO^T, P^T and dS^T with the query across lanes, and
 //     dQ^T += K^T dS^T with K^T read transposed out of the K tile and dS^T
 //     used straight from registers.
 // dQ is computed by its own pass instead of float atomics from the dK/dV
 // pass: two more contractions (7 instead of 5) but no read-modify-write
-// traffic through memory, and every output is deterministic.
+// traffic through memory, and every output is deterministic. (Float atomic
+// adds are performed past the XCD's L2, at ~1.3 TB/s of payload: the dQ
+// partials of a one-pass design alone took longer than this whole pass on
+// B8 H16 N4096 d128 causal, 1.7 ms with 256-key blocks against 0.75 ms.)
 // Q, dO, K and V tiles go HBM -> LDS with global_load_lds_dwordx4 into
 // double-buffered, XOR-swizzled (tile_swz) row-major buffers.
 
