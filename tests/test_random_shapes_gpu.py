@@ -11,6 +11,9 @@ Tolerances are the suite's own (see test_parity_gpu):
                    LSE max-abs <= 1e-3
   16-bit backward  dQ, dK, dV max-abs <= 5e-2 and relative Frobenius <= 1e-2
   fp32 forward     O and LSE max-abs <= 1e-5
+  fp8 forward      O relative Frobenius <= 5e-2 against the oracle on the
+                   dequantised codes, LSE |error| <= 1e-3 * max(1, |LSE|)
+                   (d = 128, the fp8 path's head dim; scale 1/sqrt(d))
 The eight-wave forward, which fa_fwd picks only once a launch has a
 workgroup per CU, is forced through fa_fwd_waves on the 16-bit cases it
 supports (d <= 128) so that its ragged and causal edges are reached at these
@@ -48,6 +51,7 @@ def _draw_cases(n, seed, dtypes, dims):
 
 CASES_16 = _draw_cases(28, 20261203, ["bf16", "f16"], [64, 128, 256])
 CASES_32 = _draw_cases(8, 20261204, ["f32"], [64, 128])
+CASES_8 = _draw_cases(8, 20261205, ["e4m3"], [128])
 
 
 def _cid(c):
@@ -107,3 +111,18 @@ def test_random_shape_fwd_f32(gpu_lib, c):
     o_ref, l_ref = oracle.attention_forward(to64(q), to64(k), to64(v), scale, c["causal"])
     assert max_abs(to64(o), o_ref) <= 1e-5
     assert max_abs(to64(lse), l_ref) <= 1e-5
+
+
+@pytest.mark.parametrize("c", CASES_8, ids=_cid)
+def test_random_shape_fwd_fp8(gpu_lib, c):
+    note(f"random {_cid(c)} seed={c['seed']}")
+    B, H, N, d = c["B"], c["H"], c["N"], c["d"]
+    (q8, k8, v8), scales = inputs.draw_fp8(B, H, N, d, c["seed"])
+    o, lse = gpu_lib.forward_fp8(q8.cuda(), k8.cuda(), v8.cuda(), scales, scale=d ** -0.5,
+                                 causal=c["causal"])
+    torch.cuda.synchronize()
+    q, k, v = [oracle.e4m3_decode(t.numpy()) * s for t, s in zip((q8, k8, v8), scales)]
+    o_ref, l_ref = oracle.attention_forward(q, k, v, d ** -0.5, c["causal"])
+    assert rel_frob(to64(o), o_ref) <= 5e-2
+    err = np.max(np.abs(to64(lse) - l_ref) / np.maximum(1.0, np.abs(l_ref)))
+    assert err <= 1e-3
