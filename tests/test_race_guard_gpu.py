@@ -160,3 +160,32 @@ def test_standard(gpu_lib, serial, causal):
     q, k, v = (t.cuda() for t in inputs.draw_qkv(1, 2, 1000, 128, 9800, torch.bfloat16))
     a, b = both(gpu_lib, serial, lambda: (gpu_lib.forward_standard(q, k, v, causal=causal),))
     assert_same(a, b)
+
+
+def _random_cases(n=10, seed=20261206):
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        out.append((("bf16", "f16")[int(rng.integers(2))], (64, 128, 256)[int(rng.integers(3))],
+                    bool(rng.integers(2)), int(rng.integers(1, 3)), int(rng.integers(1, 3)),
+                    int(rng.integers(300, 3001)), 9900 + i))
+    return out
+
+
+@pytest.mark.parametrize("dtype,d,causal,B,H,N,seed", _random_cases())
+def test_random_shapes(gpu_lib, serial, dtype, d, causal, B, H, N, seed):
+    """Fixed-seed random shapes with many tiles and ragged ends: forward and
+    backward of both builds bit for bit."""
+    note(f"race guard random {dtype} B{B} H{H} N{N} d{d} causal={causal} seed={seed}")
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    q, k, v, do = (t.cuda() for t in inputs.draw_qkv(B, H, N, d, seed, dt, with_do=True))
+
+    def run():
+        o, lse = gpu_lib.forward(q, k, v, causal=causal)
+        dq, dk, dv = gpu_lib.backward(q, k, v, o, lse, do, causal=causal)
+        return o, lse, dq, dk, dv
+
+    a, b = both(gpu_lib, serial, run)
+    assert_same(a, b)
+
