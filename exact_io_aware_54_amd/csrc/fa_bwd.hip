@@ -883,8 +883,10 @@ struct DqWave {
         sf[2] = pack8<T>(dp[1], 0);
         sf[3] = pack8<T>(dp[1], 8);
         // dQ^T += K^T dS^T (unit u: key group g = u / DB, b = u % DB), the
-        // transposed K operands read PT units ahead
-        constexpr int NC = 4 * C::DB, PT = D > 128 ? kPf256 : 1;
+        // transposed K operands read PT units ahead (two at d <= 128: 1.6-2.2 %
+        // faster than one on B8 H16 N4096 causal and B2 H32 N8192, same
+        // registers, bit-identical)
+        constexpr int NC = 4 * C::DB, PT = D > 128 ? kPf256 : 2;
         V8 ta[PT];
 #pragma unroll
         for (int u = 0; u < PT; ++u)
