@@ -843,8 +843,10 @@ struct DqWave {
         // K / V operand reads run PF units ahead of their MFMAs (unit t:
         // k-step t / 2, subtile t % 2), order kept by scheduling fences; one
         // ahead with the fences measured 1-2 % faster than the compiler's own
-        // order, two ahead spills in the eight-wave causal shape
-        constexpr int NU = 2 * C::KS, PF = D > 128 ? kPf256 : 1;
+        // order, two ahead another 0.6-1.5 % (B8 H16 N4096 causal, B2 H32
+        // N8192, d = 64; the eight-wave shape then needs all 256 registers,
+        // without spilling)
+        constexpr int NU = 2 * C::KS, PF = D > 128 ? kPf256 : 2;
         V8 ok[PF], ov[PF];
         auto kv_unit = [&](int t, V8& ak, V8& av) {
             const int o = roff[t >> 1] + (t & 1) * 32 * C::ROWB;
